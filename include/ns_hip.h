@@ -1,0 +1,174 @@
+/*
+ * ns_hip.h - C ABI of the MI355X (gfx950) Newton–Schulz orthogonalization
+ * library, libns_hip.so.
+ *
+ * The operation is Muon's quintic Newton–Schulz iteration applied to one
+ * matrix or to a stack of independent matrices [batch, rows, cols]:
+ *
+ *   X  <- X / (||X||_F + 1e-7)            per matrix (slice)
+ *   work on Xᵀ if rows > cols              (result returned untransposed)
+ *   repeat ns_steps times:
+ *     A = X Xᵀ,   B = b A + c A A,   X = a X + B X
+ *
+ * Sources (page title, section):
+ *   - prime-rl PR #3873 (Muon optimizer-step speedups), "Summary" item 1:
+ *     X Xᵀ and b A + c A A on a symmetric GEMM that computes one triangle and
+ *     mirrors it; a X + B X as one GEMM with the scalar folded in; fp32
+ *     alpha/beta epilogue (microbenchmark note under the NS table).
+ *   - same page, "Summary" item 2: a 3-D stack is a batch along its leading
+ *     axis; each slice is orthogonalized on its own.
+ *   - param-decomp PR #978 "stacked-NS Muon", section "What": same-shape
+ *     leaves batched into one NS; ns_steps (default 5); ns_dtype float32 or
+ *     bfloat16.
+ *   - Megatron-LM PR #6381 "Add --muon-use-syrk option ...", "Summary": the
+ *     Gram product is symmetric, so a SYRK needs about half a GEMM's FLOPs;
+ *     "Version compatibility": a requested fast path that cannot run must be
+ *     a hard error, never a silent fallback (hence the status codes below).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named in/out/x/... are DEVICE pointers on the calling thread's
+ *     current HIP device, 16-byte aligned, to contiguous row-major data.
+ *     The caller owns them; the library never frees or retains them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All work is enqueued on it; calls return after enqueueing, without a
+ *     host synchronisation.
+ *   - Argument errors are detected on the host before anything is enqueued;
+ *     no partial work is left behind.  Every call returns an ns_status.
+ *   - No entry point falls back to another implementation.
+ *   - Calls that share a device AND a stream share one library-owned
+ *     workspace and are ordered by that stream; calls on different streams
+ *     get different workspaces.
+ */
+#ifndef NS_HIP_H
+#define NS_HIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+typedef enum {
+  NS_OK = 0,
+  NS_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, ns_steps < 0,
+                             rows*cols >= 2^31, partial overlap in/out    */
+  NS_ERR_DTYPE = 2,       /* dtype is not NS_DTYPE_F32 / NS_DTYPE_BF16    */
+  NS_ERR_ALIGNMENT = 3,   /* rows or cols not a multiple of 8, or a pointer
+                             not 16-byte aligned (16-byte rows)           */
+  NS_ERR_ARCH = 4,        /* current device is not gfx950                 */
+  NS_ERR_OOM = 5,         /* workspace allocation failed                  */
+  NS_ERR_HIP = 6          /* a HIP runtime call or launch failed;
+                             details in ns_last_error()                   */
+} ns_status;
+
+/* Storage and compute dtype of every matrix of one call. */
+enum {
+  NS_DTYPE_F32 = 0,  /* fp32 storage, fp32 MFMA, fp32 epilogues           */
+  NS_DTYPE_BF16 = 1  /* bf16 storage, bf16 MFMA with fp32 accumulation,
+                        fp32 epilogues, fp32 diagonals (see below)        */
+};
+
+/*
+ * ns_orthogonalize - the whole method on a stack of matrices.
+ *
+ *   in, out   device pointers to [batch, rows, cols] row-major, `dtype`.
+ *             out may be the same pointer as in (in-place); any other
+ *             overlap is NS_ERR_INVALID_ARG.  out always has the input's
+ *             orientation (tall inputs are NOT returned transposed).
+ *   batch     number of independent slices (0..65535; 0 enqueues nothing).
+ *   rows,cols slice shape, each > 0 and a multiple of 8.
+ *   dtype     NS_DTYPE_F32 or NS_DTYPE_BF16.
+ *   ns_steps  number of quintic steps (>= 0; 0 returns X / (||X||_F + eps)).
+ *   a, b, c   quintic coefficients (Muon's usual: 3.4445, -4.7750, 2.0315).
+ *   stream    hipStream_t as void*.
+ *
+ * Each slice is normalised by its own Frobenius norm.  An all-zero slice
+ * yields zeros.  NaN/Inf inputs propagate; they are not checked.
+ * Internally the Gram matrix A and the polynomial C = aI + bA + cAA are held
+ * as an off-diagonal matrix (zero diagonal) in `dtype` plus an fp32 diagonal
+ * vector; only lower-triangle tiles of both are computed and mirrored.
+ * The workspace (ns_workspace_bytes) is allocated on first use per
+ * (device, stream) and grown when needed; growing synchronises the device.
+ */
+int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows,
+                     int64_t cols, int dtype, int ns_steps, float a, float b,
+                     float c, void* stream);
+
+/* Bytes of library workspace one ns_orthogonalize call of this shape needs. */
+size_t ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int dtype);
+
+/* Free every cached workspace (all devices and streams).  Synchronises each
+ * device that held one.  Returns NS_OK or NS_ERR_HIP. */
+int ns_release_workspace(void);
+
+/* ---- diagnostics --------------------------------------------------------- */
+
+/* Static description of a status code. */
+const char* ns_status_string(int status);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* ns_last_error(void);
+
+/* Writes (NUL-terminated, truncated to n) a description of the kernels and
+ * tile shapes the last successful call on this thread enqueued, so that a
+ * caller can tell which path ran.  Returns the full length. */
+int ns_query_last_config(char* buf, size_t n);
+
+/*
+ * Per-kernel timing with HIP events on the launch stream.
+ * ns_timing_enable(mask): from now on, every launch of a kernel whose kind
+ * bit is set in `mask` (1 << NS_KIND_*) is bracketed by two hipEvents on its
+ * stream; 0 disables.  ns_timing_reset() drops the records.
+ * ns_timing_query(kind, &total_ms, &launches) waits for the recorded events
+ * and returns the summed kernel time and the number of launches recorded.
+ */
+enum {
+  NS_KIND_SUMSQ = 0,   /* per-slice sum of squares (norm, pass 1)        */
+  NS_KIND_SCALE = 1,   /* scale and cast (norm, pass 2)                   */
+  NS_KIND_GRAM = 2,    /* lower-triangle X Xᵀ with mirror                 */
+  NS_KIND_POLY = 3,    /* lower-triangle C = aI + bA + cAA with mirror     */
+  NS_KIND_UPDATE = 4,  /* X' = C X (or X C for tall), diagonal folded     */
+  NS_KIND_COUNT = 5
+};
+int ns_timing_enable(int mask);
+int ns_timing_reset(void);
+int ns_timing_query(int kind, double* total_ms, int64_t* launches);
+
+/* ---- single stages (the same kernels ns_orthogonalize runs) ------------- */
+/* Shapes: a slice of x is rows x cols; m = min(rows, cols).  The Gram side is
+ * the short one: A = X Xᵀ when rows <= cols, A = Xᵀ X when rows > cols. */
+
+/* X0 = x / (||x||_F + 1e-7) per slice, same shape, layout and dtype.
+ * norms (optional, may be NULL): fp32 [batch] receives ||x||_F per slice.
+ * x0 may equal x. */
+int ns_stage_normalize(const void* x, void* x0, float* norms, int64_t batch,
+                       int64_t rows, int64_t cols, int dtype, void* stream);
+
+/* Gram of each slice: a_off [batch, m, m] (dtype) receives the off-diagonal
+ * entries with exact zeros on the diagonal and is bitwise symmetric;
+ * a_diag fp32 [batch, m] receives the diagonal. */
+int ns_stage_gram(const void* x, void* a_off, float* a_diag, int64_t batch,
+                  int64_t rows, int64_t cols, int dtype, void* stream);
+
+/* C = a I + b A + c A A from A = a_off + diag(a_diag), stored the same way:
+ * c_off [batch, m, m] (zero diagonal, bitwise symmetric), c_diag fp32
+ * [batch, m].  a_off must be symmetric with a zero diagonal. */
+int ns_stage_poly(const void* a_off, const float* a_diag, void* c_off,
+                  float* c_diag, int64_t batch, int64_t m, int dtype, float a,
+                  float b, float c, void* stream);
+
+/* One update with C = c_off + diag(c_diag):
+ *   rows <= cols:  x_out = C x         (C is rows x rows)
+ *   rows >  cols:  x_out = x C         (C is cols x cols)
+ * x_out must not overlap x. */
+int ns_stage_update(const void* x, const void* c_off, const float* c_diag,
+                    void* x_out, int64_t batch, int64_t rows, int64_t cols,
+                    int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NS_HIP_H */

@@ -1,0 +1,417 @@
+// ns_api.cpp - host driver of libns_hip.so: argument checks, workspace,
+// and the sequence of launches of one Newton–Schulz call.
+//
+// One call on a [batch, rows, cols] stack enqueues 2 + 3 * ns_steps kernels
+// on the caller's stream, each covering the whole stack (the batch is part of
+// the grid, so a stack of experts is one launch per stage; prime-rl PR #3873,
+// "Summary" item 2, and param-decomp PR #978, "What").
+#include <hip/hip_runtime_api.h>
+
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/ns_hip.h"
+#include "ns_kernels.h"
+#include "ns_layout.h"
+#include "ns_plan.h"
+
+namespace {
+
+using ns::GemmArgs;
+using ns::NormArgs;
+using ns::Plan;
+using ns::make_plan;
+
+thread_local std::string t_err;
+thread_local std::string t_cfg;
+
+int fail(int status, const std::string& msg) {
+  t_err = msg;
+  return status;
+}
+
+size_t esize(int dtype) { return ns::elem_size(dtype); }
+
+int check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return NS_OK;
+  return fail(NS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------- checks
+
+int check_dtype(int dtype) {
+  if (dtype != NS_DTYPE_F32 && dtype != NS_DTYPE_BF16)
+    return fail(NS_ERR_DTYPE, "dtype must be 0 (fp32) or 1 (bf16), got " + std::to_string(dtype));
+  return NS_OK;
+}
+
+int check_shape(int64_t batch, int64_t rows, int64_t cols) {
+  if (batch < 0) return fail(NS_ERR_INVALID_ARG, "batch must be >= 0");
+  if (rows <= 0 || cols <= 0) return fail(NS_ERR_INVALID_ARG, "rows and cols must be > 0");
+  if (rows % 8 != 0 || cols % 8 != 0)
+    return fail(NS_ERR_ALIGNMENT, "rows and cols must be multiples of 8 (16-byte rows), got " +
+                                      std::to_string(rows) + "x" + std::to_string(cols));
+  if (rows * cols >= (int64_t(1) << 31))
+    return fail(NS_ERR_INVALID_ARG, "a slice must hold fewer than 2^31 elements");
+  if (batch > 65535) return fail(NS_ERR_INVALID_ARG, "batch must be <= 65535");
+  return NS_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(NS_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return fail(NS_ERR_ALIGNMENT, std::string(name) + " is not 16-byte aligned");
+  return NS_OK;
+}
+
+std::mutex g_arch_mu;
+std::map<int, int> g_arch;  // device -> NS_OK or NS_ERR_ARCH
+
+int check_arch() {
+  int dev = 0;
+  if (int s = check_hip(hipGetDevice(&dev), "hipGetDevice")) return s;
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  auto it = g_arch.find(dev);
+  if (it == g_arch.end()) {
+    hipDeviceProp_t prop;
+    if (int s = check_hip(hipGetDeviceProperties(&prop, dev), "hipGetDeviceProperties")) return s;
+    const int ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? NS_OK : NS_ERR_ARCH;
+    it = g_arch.emplace(dev, ok).first;
+    if (ok != NS_OK) t_err = std::string("device is ") + prop.gcnArchName + ", this library is built for gfx950";
+  }
+  if (it->second != NS_OK) return fail(NS_ERR_ARCH, "current device is not gfx950");
+  return NS_OK;
+}
+
+// ------------------------------------------------------------- workspace
+
+struct Ws {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, void*>, Ws> g_ws;
+
+int get_workspace(hipStream_t st, size_t bytes, char** out) {
+  int dev = 0;
+  if (int s = check_hip(hipGetDevice(&dev), "hipGetDevice")) return s;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Ws& w = g_ws[{dev, (void*)st}];
+  if (w.bytes < bytes) {
+    if (w.ptr != nullptr) {
+      // the old buffer may still be read by work queued earlier
+      if (int s = check_hip(hipDeviceSynchronize(), "hipDeviceSynchronize")) return s;
+      if (int s = check_hip(hipFree(w.ptr), "hipFree")) return s;
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return fail(NS_ERR_OOM, "workspace allocation of " + std::to_string(bytes) + " bytes failed");
+    }
+    w.ptr = p;
+    w.bytes = bytes;
+  }
+  *out = static_cast<char*>(w.ptr);
+  return NS_OK;
+}
+
+// ---------------------------------------------------------------- timing
+
+struct TimingRec {
+  int kind;
+  hipEvent_t a, b;
+};
+std::mutex g_t_mu;
+int g_t_mask = 0;
+std::vector<TimingRec> g_t_recs;
+std::vector<hipEvent_t> g_t_pool;
+
+hipEvent_t take_event() {
+  if (!g_t_pool.empty()) {
+    hipEvent_t e = g_t_pool.back();
+    g_t_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <typename F>
+hipError_t timed_launch(int kind, hipStream_t st, F&& f) {
+  std::unique_lock<std::mutex> lk(g_t_mu);
+  const bool on = (g_t_mask >> kind) & 1;
+  hipEvent_t a = nullptr, b = nullptr;
+  if (on) {
+    a = take_event();
+    b = take_event();
+    if (a && b) (void)hipEventRecord(a, st);
+  }
+  lk.unlock();
+  hipError_t e = f();
+  if (on && a && b) {
+    (void)hipEventRecord(b, st);
+    lk.lock();
+    g_t_recs.push_back(TimingRec{kind, a, b});
+  }
+  return e;
+}
+
+// ---------------------------------------------------------------- stages
+
+int run_normalize(const void* x, void* y, float* norms, const Plan& p, float* partials,
+                  hipStream_t st) {
+  const NormArgs g = ns::norm_args(p, x, y, norms, partials);
+  const int batch = (int)p.batch;
+  if (int s = check_hip(timed_launch(NS_KIND_SUMSQ, st, [&] { return ns::launch_sumsq(p.dtype, g, batch, st); }),
+                        "sum-of-squares launch"))
+    return s;
+  return check_hip(timed_launch(NS_KIND_SCALE, st, [&] { return ns::launch_scale(p.dtype, g, batch, st); }),
+                   "scale launch");
+}
+
+int launch_stage(int kind_id, const char* what, const Plan& p, const GemmArgs& g, const ns::StageKind& k,
+                 hipStream_t st) {
+  return check_hip(
+      timed_launch(kind_id, st, [&] { return ns::launch_gemm(p.dtype, k.mode, k.p_layout, k.q_layout, g, st); }),
+      what);
+}
+
+int run_gram(const void* x, void* oa, float* da, const Plan& p, hipStream_t st) {
+  ns::StageKind k;
+  const GemmArgs g = ns::gram_args(p, x, oa, da, &k);
+  return launch_stage(NS_KIND_GRAM, "gram launch", p, g, k, st);
+}
+
+int run_poly(const void* oa, const float* da, void* oc, float* dc, const Plan& p, float a, float b,
+             float c, hipStream_t st) {
+  ns::StageKind k;
+  const GemmArgs g = ns::poly_args(p, oa, da, oc, dc, a, b, c, &k);
+  return launch_stage(NS_KIND_POLY, "poly launch", p, g, k, st);
+}
+
+int run_update(const void* x, const void* oc, const float* dc, void* xo, const Plan& p,
+               hipStream_t st) {
+  ns::StageKind k;
+  const GemmArgs g = ns::update_args(p, x, oc, dc, xo, &k);
+  return launch_stage(NS_KIND_UPDATE, "update launch", p, g, k, st);
+}
+
+void record_config(const Plan& p, int steps) {
+  const ns::TileCfg t = ns::tile_cfg(p.dtype);
+  char buf[512];
+  std::snprintf(buf, sizeof(buf),
+                "dtype=%s batch=%lld rows=%lld cols=%lld m=%lld %s steps=%d | norm: sumsq+scale chunk=%lldx16B | "
+                "mfma=%s tile=%dx%d threads=%d | gram=lower-tri(%s) poly=lower-tri | update=%s",
+                p.dtype == NS_DTYPE_BF16 ? "bf16" : "fp32", (long long)p.batch, (long long)p.rows,
+                (long long)p.cols, (long long)p.m, p.tall ? "tall" : "wide", steps, ns::kNormChunkVecs,
+                p.dtype == NS_DTYPE_BF16 ? "32x32x16_bf16" : "32x32x2_f32", t.bm, t.bn, t.wm * t.wn * 64,
+                p.tall ? "columns" : "rows", p.tall ? "X*C" : "C*X");
+  t_cfg = buf;
+}
+
+int common_checks(int64_t batch, int64_t rows, int64_t cols, int dtype) {
+  if (int s = check_dtype(dtype)) return s;
+  return check_shape(batch, rows, cols);
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+
+extern "C" {
+
+int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows, int64_t cols, int dtype,
+                     int ns_steps, float a, float b, float c, void* stream) {
+  t_err.clear();
+  if (int s = common_checks(batch, rows, cols, dtype)) return s;
+  if (ns_steps < 0) return fail(NS_ERR_INVALID_ARG, "ns_steps must be >= 0");
+  if (int s = check_ptr(in, "in")) return s;
+  if (int s = check_ptr(out, "out")) return s;
+  const size_t bytes = (size_t)batch * rows * cols * esize(dtype);
+  if (in != out && overlaps(in, bytes, out, bytes))
+    return fail(NS_ERR_INVALID_ARG, "out overlaps in without being the same pointer");
+  if (batch == 0) return NS_OK;
+  if (int s = check_arch()) return s;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Plan p = make_plan(batch, rows, cols, dtype);
+  char* ws = nullptr;
+  if (int s = get_workspace(st, p.total, &ws)) return s;
+  void* xtmp = ws + p.off_xtmp;
+  void* oa = ws + p.off_oa;
+  void* oc = ws + p.off_oc;
+  float* da = reinterpret_cast<float*>(ws + p.off_da);
+  float* dc = reinterpret_cast<float*>(ws + p.off_dc);
+  float* part = reinterpret_cast<float*>(ws + p.off_part);
+
+  auto buf = [&](int s) -> void* { return ns::iterate_in_out(ns_steps, s) ? out : xtmp; };
+
+  if (int s = run_normalize(in, buf(0), nullptr, p, part, st)) return s;
+  for (int s = 1; s <= ns_steps; ++s) {
+    if (int e = run_gram(buf(s - 1), oa, da, p, st)) return e;
+    if (int e = run_poly(oa, da, oc, dc, p, a, b, c, st)) return e;
+    if (int e = run_update(buf(s - 1), oc, dc, buf(s), p, st)) return e;
+  }
+  record_config(p, ns_steps);
+  return NS_OK;
+}
+
+size_t ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int dtype) {
+  if (check_dtype(dtype) != NS_OK || check_shape(batch, rows, cols) != NS_OK) return 0;
+  return make_plan(batch, rows, cols, dtype).total;
+}
+
+int ns_release_workspace(void) {
+  t_err.clear();
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  int status = NS_OK;
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  for (auto& kv : g_ws) {
+    if (kv.second.ptr == nullptr) continue;
+    if (hipSetDevice(kv.first.first) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      if (hipFree(kv.second.ptr) != hipSuccess) status = fail(NS_ERR_HIP, "hipFree failed");
+    }
+  }
+  g_ws.clear();
+  (void)hipSetDevice(cur);
+  return status;
+}
+
+const char* ns_status_string(int status) {
+  switch (status) {
+    case NS_OK: return "NS_OK";
+    case NS_ERR_INVALID_ARG: return "NS_ERR_INVALID_ARG: invalid argument";
+    case NS_ERR_DTYPE: return "NS_ERR_DTYPE: unsupported dtype";
+    case NS_ERR_ALIGNMENT: return "NS_ERR_ALIGNMENT: dims must be multiples of 8, pointers 16-byte aligned";
+    case NS_ERR_ARCH: return "NS_ERR_ARCH: device is not gfx950";
+    case NS_ERR_OOM: return "NS_ERR_OOM: workspace allocation failed";
+    case NS_ERR_HIP: return "NS_ERR_HIP: HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* ns_last_error(void) { return t_err.c_str(); }
+
+int ns_query_last_config(char* buf, size_t n) {
+  if (buf != nullptr && n > 0) {
+    std::strncpy(buf, t_cfg.c_str(), n - 1);
+    buf[n - 1] = '\0';
+  }
+  return (int)t_cfg.size();
+}
+
+int ns_timing_enable(int mask) {
+  std::lock_guard<std::mutex> lk(g_t_mu);
+  g_t_mask = mask;
+  return NS_OK;
+}
+
+int ns_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_t_mu);
+  for (auto& r : g_t_recs) {
+    g_t_pool.push_back(r.a);
+    g_t_pool.push_back(r.b);
+  }
+  g_t_recs.clear();
+  return NS_OK;
+}
+
+int ns_timing_query(int kind, double* total_ms, int64_t* launches) {
+  t_err.clear();
+  if (kind < 0 || kind >= NS_KIND_COUNT || total_ms == nullptr || launches == nullptr)
+    return fail(NS_ERR_INVALID_ARG, "bad timing query");
+  std::lock_guard<std::mutex> lk(g_t_mu);
+  double sum = 0.0;
+  int64_t count = 0;
+  for (auto& r : g_t_recs) {
+    if (r.kind != kind) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) return fail(NS_ERR_HIP, "hipEventSynchronize failed");
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(NS_ERR_HIP, "hipEventElapsedTime failed");
+    sum += ms;
+    ++count;
+  }
+  *total_ms = sum;
+  *launches = count;
+  return NS_OK;
+}
+
+int ns_stage_normalize(const void* x, void* x0, float* norms, int64_t batch, int64_t rows, int64_t cols,
+                       int dtype, void* stream) {
+  t_err.clear();
+  if (int s = common_checks(batch, rows, cols, dtype)) return s;
+  if (int s = check_ptr(x, "x")) return s;
+  if (int s = check_ptr(x0, "x0")) return s;
+  const size_t bytes = (size_t)batch * rows * cols * esize(dtype);
+  if (x != x0 && overlaps(x, bytes, x0, bytes)) return fail(NS_ERR_INVALID_ARG, "x0 overlaps x");
+  if (batch == 0) return NS_OK;
+  if (int s = check_arch()) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Plan p = make_plan(batch, rows, cols, dtype);
+  char* ws = nullptr;
+  if (int s = get_workspace(st, p.total, &ws)) return s;
+  return run_normalize(x, x0, norms, p, reinterpret_cast<float*>(ws + p.off_part), st);
+}
+
+int ns_stage_gram(const void* x, void* a_off, float* a_diag, int64_t batch, int64_t rows, int64_t cols,
+                  int dtype, void* stream) {
+  t_err.clear();
+  if (int s = common_checks(batch, rows, cols, dtype)) return s;
+  if (int s = check_ptr(x, "x")) return s;
+  if (int s = check_ptr(a_off, "a_off")) return s;
+  if (int s = check_ptr(a_diag, "a_diag")) return s;
+  if (batch == 0) return NS_OK;
+  if (int s = check_arch()) return s;
+  const Plan p = make_plan(batch, rows, cols, dtype);
+  return run_gram(x, a_off, a_diag, p, static_cast<hipStream_t>(stream));
+}
+
+int ns_stage_poly(const void* a_off, const float* a_diag, void* c_off, float* c_diag, int64_t batch, int64_t m,
+                  int dtype, float a, float b, float c, void* stream) {
+  t_err.clear();
+  if (int s = common_checks(batch, m, m, dtype)) return s;
+  if (int s = check_ptr(a_off, "a_off")) return s;
+  if (int s = check_ptr(a_diag, "a_diag")) return s;
+  if (int s = check_ptr(c_off, "c_off")) return s;
+  if (int s = check_ptr(c_diag, "c_diag")) return s;
+  const size_t bytes = (size_t)batch * m * m * esize(dtype);
+  if (overlaps(a_off, bytes, c_off, bytes)) return fail(NS_ERR_INVALID_ARG, "c_off overlaps a_off");
+  if (batch == 0) return NS_OK;
+  if (int s = check_arch()) return s;
+  const Plan p = make_plan(batch, m, m, dtype);
+  return run_poly(a_off, a_diag, c_off, c_diag, p, a, b, c, static_cast<hipStream_t>(stream));
+}
+
+int ns_stage_update(const void* x, const void* c_off, const float* c_diag, void* x_out, int64_t batch,
+                    int64_t rows, int64_t cols, int dtype, void* stream) {
+  t_err.clear();
+  if (int s = common_checks(batch, rows, cols, dtype)) return s;
+  if (int s = check_ptr(x, "x")) return s;
+  if (int s = check_ptr(c_off, "c_off")) return s;
+  if (int s = check_ptr(c_diag, "c_diag")) return s;
+  if (int s = check_ptr(x_out, "x_out")) return s;
+  const size_t bytes = (size_t)batch * rows * cols * esize(dtype);
+  if (overlaps(x, bytes, x_out, bytes)) return fail(NS_ERR_INVALID_ARG, "x_out overlaps x");
+  if (batch == 0) return NS_OK;
+  if (int s = check_arch()) return s;
+  const Plan p = make_plan(batch, rows, cols, dtype);
+  return run_update(x, c_off, c_diag, x_out, p, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

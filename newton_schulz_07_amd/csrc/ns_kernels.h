@@ -1,0 +1,16 @@
+// ns_kernels.h - launch interface between the host driver and the kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "ns_layout.h"
+
+namespace ns {
+
+hipError_t launch_gemm(int dtype, int mode, int p_layout, int q_layout, const GemmArgs& g,
+                       hipStream_t st);
+hipError_t launch_sumsq(int dtype, const NormArgs& g, int batch, hipStream_t st);
+hipError_t launch_scale(int dtype, const NormArgs& g, int batch, hipStream_t st);
+
+}  // namespace ns

@@ -1,0 +1,174 @@
+// ns_plan.h - workspace layout of one call and the launch arguments of each
+// stage.  Plain C++ (no HIP types) so that the host-side bounds checker
+// builds exactly the arguments the driver passes to the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ns_layout.h"
+
+namespace ns {
+
+constexpr float kNormEps = 1e-7f;             // added to the Frobenius norm
+constexpr long long kNormChunkVecs = 2048;    // 16-byte vectors per norm block (32 KiB)
+constexpr size_t kWsAlign = 256;
+
+inline size_t elem_size(int dtype) { return dtype == 1 ? 2 : 4; }
+inline size_t ws_align(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+inline int tiles_of(int64_t extent, int tile) { return (int)((extent + tile - 1) / tile); }
+
+// One call on [batch, rows, cols].  The Gram side is m = min(rows, cols).
+struct Plan {
+  int64_t batch, rows, cols, m, n;
+  bool tall;
+  int dtype;
+  int norm_chunks;
+  // workspace offsets (bytes)
+  size_t off_xtmp, off_oa, off_oc, off_da, off_dc, off_part, total;
+};
+
+inline Plan make_plan(int64_t batch, int64_t rows, int64_t cols, int dtype) {
+  Plan p{};
+  p.batch = batch;
+  p.rows = rows;
+  p.cols = cols;
+  p.tall = rows > cols;
+  p.m = p.tall ? cols : rows;
+  p.n = p.tall ? rows : cols;
+  p.dtype = dtype;
+  const size_t es = elem_size(dtype);
+  const long long vecs = rows * cols * (long long)es / 16;
+  p.norm_chunks = (int)((vecs + kNormChunkVecs - 1) / kNormChunkVecs);
+  size_t off = 0;
+  p.off_xtmp = off;
+  off += ws_align((size_t)batch * rows * cols * es);
+  p.off_oa = off;
+  off += ws_align((size_t)batch * p.m * p.m * es);
+  p.off_oc = off;
+  off += ws_align((size_t)batch * p.m * p.m * es);
+  p.off_da = off;
+  off += ws_align((size_t)batch * p.m * 4);
+  p.off_dc = off;
+  off += ws_align((size_t)batch * p.m * 4);
+  p.off_part = off;
+  off += ws_align((size_t)batch * p.norm_chunks * 4);
+  p.total = off;
+  return p;
+}
+
+// The iterate X_s (s = 0 after normalisation) is held in `out` when
+// (steps - s) is even and in the workspace temporary otherwise, so the last
+// step writes `out` and no update reads the buffer it writes.
+inline bool iterate_in_out(int steps, int s) { return ((steps - s) % 2) == 0; }
+
+inline NormArgs norm_args(const Plan& p, const void* x, void* y, float* norms, float* partials) {
+  NormArgs g{};
+  g.x = x;
+  g.y = y;
+  g.partials = partials;
+  g.norms = norms;
+  g.slice_vecs = p.rows * p.cols * (long long)elem_size(p.dtype) / 16;
+  g.chunk_vecs = kNormChunkVecs;
+  g.chunks = p.norm_chunks;
+  g.eps = kNormEps;
+  return g;
+}
+
+// Which operand loaders a stage uses.
+struct StageKind {
+  int mode, p_layout, q_layout;
+};
+
+// A = X Xᵀ (rows <= cols: rows of X) or Xᵀ X (rows > cols: columns of X).
+inline GemmArgs gram_args(const Plan& p, const void* x, void* oa, float* da, StageKind* kind) {
+  const TileCfg t = tile_cfg(p.dtype);
+  GemmArgs g{};
+  g.P = g.Q = x;
+  g.p_bs = g.q_bs = p.rows * p.cols;
+  g.ldp = g.ldq = (int)p.cols;
+  g.M = g.N = (int)p.m;
+  g.K = (int)p.n;
+  g.tiles_m = g.tiles_n = tiles_of(p.m, t.bm);
+  g.tiles_per_slice = g.tiles_m * (g.tiles_m + 1) / 2;
+  g.batch = (int)p.batch;
+  g.out = oa;
+  g.o_bs = p.m * p.m;
+  g.ldo = (int)p.m;
+  g.d_out = da;
+  g.d_bs = p.m;
+  const int layout = p.tall ? MCONT : KCONT;
+  *kind = StageKind{MODE_GRAM, layout, layout};
+  return g;
+}
+
+// C = a I + b A + c A A from the split A, written split the same way.
+inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* oc, float* dc, float a,
+                          float b, float c, StageKind* kind) {
+  const TileCfg t = tile_cfg(p.dtype);
+  GemmArgs g{};
+  g.P = g.Q = oa;
+  g.p_bs = g.q_bs = p.m * p.m;
+  g.ldp = g.ldq = (int)p.m;
+  g.M = g.N = g.K = (int)p.m;
+  g.tiles_m = g.tiles_n = tiles_of(p.m, t.bm);
+  g.tiles_per_slice = g.tiles_m * (g.tiles_m + 1) / 2;
+  g.batch = (int)p.batch;
+  g.out = oc;
+  g.o_bs = p.m * p.m;
+  g.ldo = (int)p.m;
+  g.E = oa;
+  g.e_bs = p.m * p.m;
+  g.lde = (int)p.m;
+  g.d_in = da;
+  g.d_out = dc;
+  g.d_bs = p.m;
+  g.ca = a;
+  g.cb = b;
+  g.cc = c;
+  *kind = StageKind{MODE_POLY, KCONT, KCONT};
+  return g;
+}
+
+// X' = C X (rows <= cols) or X C (rows > cols), C = O_C + diag(d_C).
+inline GemmArgs update_args(const Plan& p, const void* x, const void* oc, const float* dc, void* xo,
+                            StageKind* kind) {
+  const TileCfg t = tile_cfg(p.dtype);
+  GemmArgs g{};
+  if (!p.tall) {  // P = rows of O_C, Q = columns of X
+    g.P = oc;
+    g.p_bs = p.m * p.m;
+    g.ldp = (int)p.m;
+    g.Q = x;
+    g.q_bs = p.rows * p.cols;
+    g.ldq = (int)p.cols;
+    *kind = StageKind{MODE_UPD_ROW, KCONT, MCONT};
+  } else {  // P = rows of X, Q = rows of O_C (C is symmetric)
+    g.P = x;
+    g.p_bs = p.rows * p.cols;
+    g.ldp = (int)p.cols;
+    g.Q = oc;
+    g.q_bs = p.m * p.m;
+    g.ldq = (int)p.m;
+    *kind = StageKind{MODE_UPD_COL, KCONT, KCONT};
+  }
+  g.M = (int)p.rows;
+  g.N = (int)p.cols;
+  g.K = (int)p.m;
+  g.tiles_m = tiles_of(p.rows, t.bm);
+  g.tiles_n = tiles_of(p.cols, t.bn);
+  g.tiles_per_slice = g.tiles_m * g.tiles_n;
+  g.batch = (int)p.batch;
+  g.out = xo;
+  g.o_bs = p.rows * p.cols;
+  g.ldo = (int)p.cols;
+  g.E = x;
+  g.e_bs = p.rows * p.cols;
+  g.lde = (int)p.cols;
+  g.d_in = dc;
+  g.d_out = nullptr;
+  g.d_bs = p.m;
+  return g;
+}
+
+}  // namespace ns

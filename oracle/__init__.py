@@ -11,6 +11,9 @@ from .ns_oracle import (  # noqa: F401
     EPS,
     frobenius_normalize,
     ns_iteration,
+    gram_matrix,
+    poly_matrix,
+    apply_update,
     newton_schulz,
     newton_schulz_batched,
     dense_equivalent_flops,

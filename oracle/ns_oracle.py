@@ -56,6 +56,28 @@ def ns_iteration(x, a, b, c):
     return a * x + B @ x
 
 
+def gram_matrix(x):
+    """A = X Xᵀ of a wide (or square) matrix; Xᵀ X of a tall one (step 1 above
+    applied: the Gram side is always the short side)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x.T @ x if x.shape[0] > x.shape[1] else x @ x.T
+
+
+def poly_matrix(A, a, b, c):
+    """C = a I + b A + c A A: the step's left factor, since aX + BX = (aI + B) X
+    with B = bA + cAA (step 3 above, regrouped)."""
+    A = np.asarray(A, dtype=np.float64)
+    return a * np.eye(A.shape[0]) + b * A + c * (A @ A)
+
+
+def apply_update(x, C):
+    """X' = C X for a wide X; X' = X C for a tall X (the transpose of
+    Cᵀ Xᵀ = C Xᵀ, C symmetric), so a tall X is updated without transposing."""
+    x = np.asarray(x, dtype=np.float64)
+    C = np.asarray(C, dtype=np.float64)
+    return x @ C if x.shape[0] > x.shape[1] else C @ x
+
+
 def newton_schulz(x, steps=DEFAULT_STEPS, coeffs=DEFAULT_COEFFS, eps=EPS):
     """Orthogonalize one 2-D matrix; returns float64 of the input's shape."""
     X = np.array(x, dtype=np.float64, copy=True)

@@ -1,0 +1,121 @@
+"""The C ABI library without a GPU: it loads, exports every declared symbol,
+rejects bad arguments on the host before touching the device, and its
+launch grids and indexes stay inside their buffers (host-side replay)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import newton_schulz_07_amd as ns
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ns_hip.h")
+FAKE_IN = 0x10000000
+FAKE_OUT = 0x20000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ns_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_what_the_binding_wraps():
+    assert declared_functions() == sorted(ns.SIGNATURES)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = ns.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def call(batch=1, rows=256, cols=512, dtype=1, steps=5, inp=FAKE_IN, out=FAKE_OUT):
+    return ns.lib().ns_orthogonalize(ctypes.c_void_p(inp), ctypes.c_void_p(out), batch, rows, cols, dtype,
+                                     steps, 3.4445, -4.775, 2.0315, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(inp=0), 1),                      # NULL in
+    (dict(out=0), 1),                      # NULL out
+    (dict(rows=0), 1),
+    (dict(cols=-8), 1),
+    (dict(batch=-1), 1),
+    (dict(steps=-1), 1),
+    (dict(rows=65536, cols=65536), 1),     # slice of 2^32 elements
+    (dict(dtype=2), 2),
+    (dict(dtype=-1), 2),
+    (dict(rows=260), 3),                   # not a multiple of 8
+    (dict(cols=100), 3),
+    (dict(inp=FAKE_IN + 8), 3),            # not 16-byte aligned
+    (dict(out=FAKE_IN + 256 * 512), 1),    # partial overlap with in
+])
+def test_argument_errors_are_reported_before_any_launch(kwargs, status):
+    st = call(**kwargs)
+    assert st == status
+    assert ns.lib().ns_last_error().decode() != ""
+    assert ns.lib().ns_status_string(st).decode().startswith("NS_ERR")
+
+
+def test_empty_batch_is_a_no_op():
+    assert call(batch=0) == 0
+    assert call(batch=0, inp=FAKE_IN, out=FAKE_IN) == 0
+
+
+def test_stage_argument_errors():
+    L = ns.lib()
+    vp = ctypes.c_void_p
+    assert L.ns_stage_gram(vp(FAKE_IN), vp(0), vp(FAKE_OUT), 1, 64, 64, 1, None) == 1
+    assert L.ns_stage_poly(vp(FAKE_IN), vp(FAKE_OUT), vp(FAKE_IN), vp(FAKE_OUT), 1, 64, 1, 1.0, 0.0, 0.0, None) == 1
+    assert L.ns_stage_update(vp(FAKE_IN), vp(FAKE_OUT), vp(FAKE_OUT + 1 << 20), vp(FAKE_IN), 1, 64, 64, 1, None) == 1
+    assert L.ns_stage_normalize(vp(FAKE_IN), vp(FAKE_OUT), None, 1, 63, 64, 1, None) == 3
+    assert L.ns_stage_normalize(vp(FAKE_IN), vp(FAKE_OUT), None, 0, 64, 64, 1, None) == 0
+
+
+def test_workspace_bytes():
+    L = ns.lib()
+    # temporary X + two m x m matrices + two fp32 diagonals + norm partials
+    b, r, c = 128, 1536, 2048
+    ws = L.ns_workspace_bytes(b, r, c, 1)
+    assert ws >= b * r * c * 2 + 2 * b * r * r * 2 + 2 * b * r * 4
+    assert ws < 1.01 * (b * r * c * 2 + 2 * b * r * r * 2) + (1 << 20)
+    assert L.ns_workspace_bytes(1, 14336, 4096, 1) == L.ns_workspace_bytes(1, 4096, 14336, 1)
+    assert L.ns_workspace_bytes(1, 10, 16, 1) == 0  # invalid shape
+    assert L.ns_workspace_bytes(1, 16, 16, 7) == 0  # invalid dtype
+
+
+def test_timing_query_rejects_bad_kind():
+    L = ns.lib()
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert L.ns_timing_query(99, ctypes.byref(ms), ctypes.byref(n)) == 1
+    assert L.ns_timing_reset() == 0
+    assert L.ns_timing_query(2, ctypes.byref(ms), ctypes.byref(n)) == 0 and n.value == 0
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        ns.orthogonalize(torch.zeros(8, 8))
+
+
+@pytest.fixture(scope="module")
+def boundscheck():
+    import __graft_entry__
+    return __graft_entry__.build_boundscheck()
+
+
+@pytest.mark.parametrize("case", [
+    "1 1 256 512 5", "0 1 256 512 5",        # the small workload, both dtypes
+    "1 3 264 520 5", "0 3 264 520 3",        # ragged tails, batch, wide
+    "1 2 520 264 4", "0 2 520 264 1",        # tall
+    "1 1 8 8 1", "1 1 8 2048 5", "1 4 2048 8 2", "1 1 136 136 5",
+    "1 1 40 24 0",                           # zero steps
+    "1 16 384 512 5", "1 2 1040 336 5",      # batched, tall, several tiles
+])
+def test_launch_indexes_stay_in_bounds(boundscheck, case):
+    r = subprocess.run([boundscheck] + case.split(), capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "violations=0" in r.stdout

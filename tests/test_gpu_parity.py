@@ -1,0 +1,154 @@
+"""End-to-end parity of ns_orthogonalize with the fp64 oracle on small and
+ragged inputs, plus determinism, batch invariance and in-place use.
+
+Bars: relative Frobenius error per slice <= 1e-4 for the fp32 path and
+<= 1e-2 for the bf16 path (bf16 MFMA, fp32 accumulation and epilogues).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import newton_schulz_07_amd as ns
+from ns_inputs import gaussian, make_workload
+from oracle import newton_schulz, newton_schulz_batched
+from tests.gpu_util import device, rel_err, report, to64
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [(3, 264, 520), (2, 520, 264), (1, 8, 8), (1, 8, 2048), (4, 2048, 8), (2, 136, 1032),
+         (1, 1032, 136), (1, 512, 512), (5, 64, 96)]
+
+
+def test_iid_256x512_fp32_and_bf16():
+    dev = device()
+    x = make_workload("iid_256x512")
+    ref = newton_schulz(x.double().numpy())
+    y32 = ns.orthogonalize(x.to(dev))
+    y16 = ns.orthogonalize(x.to(torch.bfloat16).to(dev))  # the cast is charged to the bf16 path
+    torch.cuda.synchronize()
+    e32, e16 = rel_err(to64(y32), ref)[0], rel_err(to64(y16), ref)[0]
+    report({"case": "iid_256x512", "fp32": e32, "bf16": e16})
+    assert e32 <= 1e-4
+    assert e16 <= 1e-2
+    assert y16.dtype == torch.bfloat16 and y16.shape == x.shape
+
+
+@pytest.mark.parametrize("shape", SMALL)
+def test_small_shapes_fp32(shape):
+    dev = device()
+    x = gaussian(shape, 500 + sum(shape), torch.float32)
+    ref = newton_schulz_batched(x.double().numpy())
+    y = ns.orthogonalize(x.to(dev))
+    torch.cuda.synchronize()
+    e = rel_err(to64(y), ref)
+    report({"case": f"small_fp32_{shape}", "max": float(e.max())})
+    assert e.max() <= 1e-4
+
+
+@pytest.mark.parametrize("shape", SMALL)
+def test_small_shapes_bf16(shape):
+    dev = device()
+    x = gaussian(shape, 600 + sum(shape), torch.bfloat16)
+    ref = newton_schulz_batched(x.double().numpy())
+    y = ns.orthogonalize(x.to(dev))
+    torch.cuda.synchronize()
+    e = rel_err(to64(y), ref)
+    report({"case": f"small_bf16_{shape}", "max": float(e.max())})
+    assert e.max() <= 1e-2
+
+
+@pytest.mark.parametrize("steps", [0, 1, 2, 3, 4, 5, 7])
+def test_step_counts(steps):
+    dev = device()
+    x = gaussian((2, 136, 264), 700 + steps, torch.float32)
+    ref = newton_schulz_batched(x.double().numpy(), steps=steps)
+    y = ns.orthogonalize(x.to(dev), steps=steps)
+    torch.cuda.synchronize()
+    assert rel_err(to64(y), ref).max() <= 1e-4
+
+
+def test_other_coefficients():
+    dev = device()
+    x = gaussian((2, 72, 136), 710, torch.float32)
+    coeffs = (1.5, -0.5, 0.0)
+    ref = newton_schulz_batched(x.double().numpy(), steps=9, coeffs=coeffs)
+    y = ns.orthogonalize(x.to(dev), steps=9, coeffs=coeffs)
+    torch.cuda.synchronize()
+    assert rel_err(to64(y), ref).max() <= 1e-4
+
+
+def test_zero_slice_gives_zeros_and_scales_are_per_slice():
+    dev = device()
+    x = gaussian((3, 64, 128), 720, torch.float32)
+    x[1] = 0
+    x[2] *= 1e-3
+    y = ns.orthogonalize(x.to(dev))
+    torch.cuda.synchronize()
+    assert torch.all(y[1] == 0)
+    ref = newton_schulz_batched(x.double().numpy())
+    assert rel_err(to64(y[[0, 2]]), ref[[0, 2]]).max() <= 1e-4
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_in_place(dtype):
+    dev = device()
+    x = gaussian((2, 136, 264), 730, dtype).to(dev)
+    want = ns.orthogonalize(x.clone())
+    ns.orthogonalize(x, out=x)
+    for steps in (0, 1, 4):
+        z = gaussian((2, 136, 264), 731 + steps, dtype).to(dev)
+        w = ns.orthogonalize(z.clone(), steps=steps)
+        ns.orthogonalize(z, steps=steps, out=z)
+        assert torch.equal(z, w)
+    torch.cuda.synchronize()
+    assert torch.equal(x, want)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_deterministic_and_batch_invariant(dtype):
+    dev = device()
+    x = gaussian((6, 264, 392), 740, dtype).to(dev)
+    y1 = ns.orthogonalize(x)
+    y2 = ns.orthogonalize(x)
+    assert torch.equal(y1, y2), "two runs differ"
+    for i in (0, 3, 5):
+        yi = ns.orthogonalize(x[i:i + 1].contiguous())
+        assert torch.equal(yi[0], y1[i]), f"slice {i} differs from its single-slice call"
+    xt = x.transpose(1, 2).contiguous()
+    yt = ns.orthogonalize(xt)
+    torch.cuda.synchronize()
+    # tall input: same result transposed, to rounding (different reduction order)
+    e = rel_err(to64(yt.transpose(1, 2)), to64(y1))
+    assert e.max() <= (1e-6 if dtype == torch.float32 else 1e-2)
+
+
+def test_errors_raise_and_do_not_fall_back():
+    dev = device()
+    with pytest.raises(ns.NSError):
+        ns.orthogonalize(torch.zeros(12, 16, device=dev))  # 12 is not a multiple of 8
+    with pytest.raises(TypeError):
+        ns.orthogonalize(torch.zeros(16, 16, device=dev, dtype=torch.float16))
+
+
+def test_config_query_names_the_kernels():
+    dev = device()
+    ns.orthogonalize(gaussian((2, 64, 128), 750, torch.bfloat16).to(dev))
+    cfg = ns.ns_query_last_config()
+    assert "mfma=32x32x16_bf16" in cfg and "gram=lower-tri" in cfg and "batch=2" in cfg
+
+
+def test_timing_records_each_launch():
+    dev = device()
+    x = gaussian((2, 256, 512), 760, torch.bfloat16).to(dev)
+    ns.ns_timing_reset()
+    ns.ns_timing_enable(0x1f)
+    try:
+        ns.orthogonalize(x, steps=3)
+    finally:
+        ns.ns_timing_enable(0)
+    for kind, n in ((ns.NS_KIND_SUMSQ, 1), (ns.NS_KIND_SCALE, 1), (ns.NS_KIND_GRAM, 3),
+                    (ns.NS_KIND_POLY, 3), (ns.NS_KIND_UPDATE, 3)):
+        ms, cnt = ns.ns_timing_query(kind)
+        assert cnt == n and ms > 0
+    ns.ns_timing_reset()

@@ -306,3 +306,20 @@ def test_flops_formula():
     assert oracle.dense_equivalent_flops(1, 4096, 4096) == 5 * 6 * 4096 ** 3
     assert oracle.dense_equivalent_flops(128, 1536, 2048) == 128 * 5 * (4 * 1536 ** 2 * 2048 + 2 * 1536 ** 3)
     assert oracle.dense_equivalent_flops(1, 14336, 4096) == oracle.dense_equivalent_flops(1, 4096, 14336)
+
+
+# ---------------------------------------------------------------- step helpers
+
+@pytest.mark.parametrize("shape", [(12, 20), (20, 12), (16, 16)])
+def test_step_helpers_compose_to_one_iteration(shape):
+    # the per-step helpers (used as references for single kernels) regroup
+    # exactly the iteration: aX + (bA + cAA)X = (aI + bA + cAA)X, and for a
+    # tall X the same step on Xᵀ, transposed back.
+    rng = np.random.default_rng(12)
+    x = ns_oracle.frobenius_normalize(rng.standard_normal(shape))
+    a, b, c = DEFAULT_COEFFS
+    C = ns_oracle.poly_matrix(ns_oracle.gram_matrix(x), a, b, c)
+    got = ns_oracle.apply_update(x, C)
+    want = ns_oracle.ns_iteration(x.T, a, b, c).T if shape[0] > shape[1] else ns_oracle.ns_iteration(x, a, b, c)
+    assert rel(got, want) <= 1e-14
+    assert ns_oracle.gram_matrix(x).shape == (min(shape), min(shape))
