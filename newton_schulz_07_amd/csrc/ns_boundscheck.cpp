@@ -64,62 +64,70 @@ void lds_index(int idx, int limit, const char* what) {
     fail(std::string(what) + ": LDS chunk " + std::to_string(idx) + " outside [0," + std::to_string(limit) + ")");
 }
 
-// One operand's loads of stage k0 for one thread (mirrors OperandLoader).
-void replay_loader(int layout, int es, int R, int NT, const void* base, long long slice_off, int ld, int r0,
-                   int rmax, int k0, int kmax, int tid, const char* what) {
+// One wave's load instructions of stage kt (mirrors issue() in gemm_kernel):
+// every lane either reads 16 in-range bytes of its operand slice or uses an
+// offset at or past the slice end (which the buffer range check turns into
+// zeros); every LDS write lands inside the stage slot.
+void replay_dma(int wave, int niw, int bm, int cpr, int es, int k0, int K, const GemmArgs& g, int slice, int i0,
+                int j0, int stage_chunks, int slot, int lds_limit, const char* what) {
   const int EPC = 16 / es;
-  if (layout == KCONT) {
-    const int NCH = R * 8, ITER = (NCH + NT - 1) / NT;
-    for (int it = 0; it < ITER; ++it) {
-      const int qd = tid + it * NT;
-      if (qd >= NCH) continue;
-      const KcontSrc s = kcont_src(qd);
-      lds_index(lds_swz(s.row, s.ch), R * 8, what);
-      const int gi = r0 + s.row, gk = k0 + s.ch * EPC;
-      if (gi < rmax && gk < kmax) access(base, (slice_off + (long long)gi * ld + gk) * es, 16, what);
-    }
-  } else {
-    const int IB = R / EPC, NBLK = IB * 8, ITER = (NBLK + NT - 1) / NT;
-    for (int it = 0; it < ITER; ++it) {
-      const int qd = tid + it * NT;
-      if (qd >= NBLK) continue;
-      const McontSrc s = mcont_src(qd, IB);
-      for (int ii = 0; ii < EPC; ++ii) lds_index(lds_swz(s.ib * EPC + ii, s.kb), R * 8, what);
-      const int gi = r0 + s.ib * EPC;
-      if (gi >= rmax) continue;
-      for (int kk = 0; kk < EPC; ++kk) {
-        const int gk = k0 + s.kb * EPC + kk;
-        if (gk < kmax) access(base, (slice_off + (long long)gk * ld + gi) * es, 16, what);
-      }
+  const unsigned kOut = 0x80000000u;
+  const long long pbytes = g.p_bs * es, qbytes = g.q_bs * es;
+  if (pbytes >= (long long)kOut || qbytes >= (long long)kOut) fail(std::string(what) + ": slice too large for the range trick");
+  for (int t = 0; t < niw; ++t) {
+    const int idx = wave * niw + t;
+    for (int lane = 0; lane < 64; ++lane) {
+      const DmaSrc d = dma_src(idx, lane, bm, cpr);
+      if ((idx * 64 < bm * cpr) != d.is_p) fail(std::string(what) + ": load instruction spans both operands");
+      lds_index(slot * stage_chunks + idx * 64 + lane, lds_limit, what);
+      if (idx * 64 + lane >= stage_chunks) fail(std::string(what) + ": load outside its stage slot");
+      const int grow = (d.is_p ? i0 : j0) + d.row;
+      const bool rowok = grow < (d.is_p ? g.M : g.N);
+      const int ld = d.is_p ? g.ldp : g.ldq;
+      const bool ok = rowok && k0 + d.ch * EPC < K;
+      if (!ok) continue;  // offset kOut: reads zeros
+      const long long off = ((long long)grow * ld + d.ch * EPC + k0) * es;
+      if (off + 16 > (d.is_p ? pbytes : qbytes) || off >= (long long)kOut)
+        fail(std::string(what) + ": in-range load past the slice");
+      access(d.is_p ? g.P : g.Q, (long long)slice * (d.is_p ? g.p_bs : g.q_bs) * es + off, 16, what);
     }
   }
 }
 
 // Replays one launch of gemm_kernel (grid = tiles_per_slice * batch).
-void replay_gemm(const GemmArgs& g, const StageKind& k, int dtype, bool coverage, const char* what) {
-  const TileCfg t = tile_cfg(dtype);
+void replay_gemm(const GemmArgs& g, int mode, int dtype, bool wide_tri, bool coverage, const char* what) {
+  const bool tri = mode_is_tri(mode);
+  const TileCfg t = tile_cfg(dtype, tri, wide_tri);
   const int es = (int)elem_size(dtype);
-  const int EPC = 16 / es, BK = 8 * EPC;
+  const int EPC = 16 / es, BK = t.cpr * EPC;
   const int NT = t.wm * t.wn * 64, WTM = t.bm / t.wm, WTN = t.bn / t.wn;
   const int SM = WTM / 32, SN = WTN / 32;
   const int G = g.tiles_per_slice * g.batch;
-  const bool tri = mode_is_tri(k.mode);
   const int nk = (g.K + BK - 1) / BK;
+  const int LP = t.bm * t.cpr, LQ = t.bn * t.cpr, STAGE = LP + LQ;
+  const int LDS = lds_chunks(t.bm, t.bn, t.cpr, t.st, es);
+  const int ERC = epi_row_chunks(t.bn, es), SROW = ERC * EPC;
+  const int NW = t.wm * t.wn, NIW = STAGE / 64 / NW;
+
+  if (t.st * STAGE > LDS) fail(std::string(what) + ": the K-stage ring does not fit the LDS array");
+  if (STAGE % (64 * NW) != 0 || LP % 64 != 0) fail(std::string(what) + ": stage does not split into wave loads");
+  if (t.bm * SROW * es > LDS * 16) fail(std::string(what) + ": staged tile does not fit the LDS array");
 
   std::vector<uint8_t> seen(G, 0);
   const long long out_elems = (long long)g.o_bs * g.batch;
-  std::vector<uint8_t> cover, dcover;
+  std::vector<uint8_t> cover, tcover, dcover;
   if (coverage) {
     cover.assign(out_elems, 0);
+    if (g.out_t && g.out_t != g.out) tcover.assign((size_t)g.ot_bs * g.batch, 0);
     if (g.d_out) dcover.assign((size_t)g.d_bs * g.batch, 0);
   }
-  // fragment reads stay inside each region (independent of the block)
+  // fragment reads stay inside each operand region of a slot
   for (int wave = 0; wave < t.wm * t.wn; ++wave)
     for (int lane = 0; lane < 64; ++lane)
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < t.cpr / 2; ++s) {
         const int ch = 2 * s + (lane >> 5), wm = wave / t.wn, wn = wave % t.wn;
-        for (int a = 0; a < SM; ++a) lds_index(lds_swz(wm * WTM + a * 32 + (lane & 31), ch), t.bm * 8, what);
-        for (int b = 0; b < SN; ++b) lds_index(lds_swz(wn * WTN + b * 32 + (lane & 31), ch), t.bn * 8, what);
+        for (int a = 0; a < SM; ++a) lds_index(lds_swz(wm * WTM + a * 32 + (lane & 31), ch, t.cpr), LP, what);
+        for (int b = 0; b < SN; ++b) lds_index(lds_swz(wn * WTN + b * 32 + (lane & 31), ch, t.cpr), LQ, what);
       }
 
   for (int w = 0; w < G; ++w) {
@@ -140,86 +148,142 @@ void replay_gemm(const GemmArgs& g, const StageKind& k, int dtype, bool coverage
     const int i0 = ti * t.bm, j0 = tj * t.bn;
     const int kstages[2] = {0, nk - 1};
     for (int si = 0; si < (nk > 1 ? 2 : 1); ++si) {
-      const int k0 = kstages[si] * BK;
-      for (int tid = 0; tid < NT; ++tid) {
-        replay_loader(k.p_layout, es, t.bm, NT, g.P, (long long)slice * g.p_bs, g.ldp, i0, g.M, k0, g.K, tid, what);
-        replay_loader(k.q_layout, es, t.bn, NT, g.Q, (long long)slice * g.q_bs, g.ldq, j0, g.N, k0, g.K, tid, what);
-      }
+      const int kt = kstages[si];
+      for (int wave = 0; wave < NW; ++wave)
+        replay_dma(wave, NIW, t.bm, t.cpr, es, kt * BK, g.K, g, slice, i0, j0, STAGE, kt % t.st, LDS, what);
     }
-    // epilogue (mirrors gemm_kernel)
+    // epilogue step 1 (mirrors gemm_kernel): registers -> staged tile
     const bool diag_tile = tri && ti == tj;
     const long long ob = (long long)slice * g.o_bs, eb = (long long)slice * g.e_bs, db = (long long)slice * g.d_bs;
+    const int qsz = 4 * es;  // bytes of 4 consecutive elements
     for (int tid = 0; tid < NT; ++tid) {
       const int lane = tid & 63, wave = tid >> 6, wm = wave / t.wn, wn = wave % t.wn;
-      for (int a = 0; a < SM; ++a)
+      for (int a = 0; a < SM; ++a) {
+        const int il = wm * WTM + a * 32 + acc_i(lane), i = i0 + il;
         for (int b = 0; b < SN; ++b)
-          for (int r = 0; r < 16; ++r) {
-            const int row = i0 + wm * WTM + a * 32 + acc_row(r, lane);
-            const int col = j0 + wn * WTN + b * 32 + acc_col(lane);
-            if (row >= g.M || col >= g.N) continue;
-            auto wr = [&](long long e) {
-              access(g.out, (ob + e) * es, es, what);
-              if (coverage && ob + e >= 0 && ob + e < out_elems) cover[ob + e]++;
-            };
-            if (tri) {
-              if (diag_tile && row < col) continue;
-              if (row == col) {
-                if (k.mode == MODE_POLY) access(g.d_in, (db + row) * 4, 4, what);
-                access(g.d_out, (db + row) * 4, 4, what);
-                if (coverage) dcover[db + row]++;
-                wr((long long)row * g.ldo + col);
-              } else {
-                if (k.mode == MODE_POLY) {
-                  access(g.E, (eb + (long long)row * g.lde + col) * es, es, what);
-                  access(g.d_in, (db + row) * 4, 4, what);
-                  access(g.d_in, (db + col) * 4, 4, what);
-                }
-                wr((long long)row * g.ldo + col);
-                wr((long long)col * g.ldo + row);
+          for (int rg = 0; rg < 4; ++rg) {
+            const int jl = wn * WTN + b * 32 + acc_j(rg, lane), j = j0 + jl;
+            if (i >= g.M || j >= g.N) continue;
+            if (j + 3 >= g.N) fail(std::string(what) + ": quad crosses N");
+            const long long sbyte = ((long long)il * SROW + jl) * es;
+            if (sbyte < 0 || sbyte + qsz > (long long)LDS * 16 || sbyte % qsz != 0)
+              fail(std::string(what) + ": staged write outside LDS or misaligned");
+            if (mode == MODE_GRAM || mode == MODE_POLY) {
+              if (mode == MODE_POLY) {
+                access(g.E, (eb + (long long)i * g.lde + j) * es, qsz, what);
+                access(g.d_in, (db + j) * 4, 16, what);
+                access(g.d_in, (db + i) * 4, 4, what);
               }
+              for (int e = 0; e < 4; ++e)
+                if (i == j + e) {
+                  access(g.d_out, (db + i) * 4, 4, what);
+                  if (coverage) dcover[db + i]++;
+                }
             } else {
-              access(g.d_in, (db + (k.mode == MODE_UPD_ROW ? row : col)) * 4, 4, what);
-              access(g.E, (eb + (long long)row * g.lde + col) * es, es, what);
-              wr((long long)row * g.ldo + col);
+              access(g.E, (eb + (long long)i * g.lde + j) * es, qsz, what);
+              access(g.d_in, (db + (mode == MODE_UPD_ROW ? i : j)) * 4, mode == MODE_UPD_ROW ? 4 : 16, what);
             }
           }
+      }
+    }
+    // step 2: direct store of tile rows
+    const int CPT = t.bn / EPC;
+    for (int qd = 0; qd < t.bm * CPT; ++qd) {
+      const int il = qd / CPT, c = qd % CPT, i = i0 + il, j = j0 + c * EPC;
+      if (i >= g.M || j >= g.N) continue;
+      if (diag_tile && c * EPC + EPC - 1 > il) {
+        for (int e = 0; e < EPC; ++e) {
+          const int jl = c * EPC + e;
+          const long long src = (jl <= il) ? (long long)il * SROW + jl : (long long)jl * SROW + il;
+          if (src * es + es > (long long)LDS * 16) fail(std::string(what) + ": mirror read outside LDS");
+        }
+      }
+      access(g.out, (ob + (long long)i * g.ldo + j) * es, 16, what);
+      if (coverage)
+        for (int e = 0; e < EPC; ++e) cover[ob + (long long)i * g.ldo + j + e]++;
+    }
+    // step 3: transposed store
+    if (g.out_t != nullptr && !diag_tile) {
+      const long long tb = (long long)slice * g.ot_bs;
+      const int RCH = t.bm / EPC;
+      for (int qd = 0; qd < t.bn * RCH; ++qd) {
+        const int jl = qd % t.bn, rc = qd / t.bn, j = j0 + jl, i = i0 + rc * EPC;
+        if (j >= g.N || i >= g.M) continue;
+        if (((long long)(rc * EPC + EPC - 1) * SROW + jl) * es + es > (long long)LDS * 16)
+          fail(std::string(what) + ": transposed read outside LDS");
+        access(g.out_t, (tb + (long long)j * g.ldt + i) * es, 16, what);
+        if (coverage) {
+          std::vector<uint8_t>& cv = (g.out_t == g.out) ? cover : tcover;
+          for (int e = 0; e < EPC; ++e) cv[tb + (long long)j * g.ldt + i + e]++;
+        }
+      }
     }
   }
   if (coverage) {
     long long bad = 0;
     for (int s = 0; s < g.batch; ++s)
       for (int i = 0; i < g.M; ++i)
-        for (int j = 0; j < g.N; ++j)
-          if (cover[(long long)s * g.o_bs + (long long)i * g.ldo + j] != 1) ++bad;
+        for (int j = 0; j < g.N; ++j) {
+          const uint8_t c = cover[(long long)s * g.o_bs + (long long)i * g.ldo + j];
+          if (c != 1) ++bad;
+          if (!tcover.empty() && tcover[(long long)s * g.ot_bs + (long long)j * g.ldt + i] != 1) ++bad;
+        }
     for (size_t i = 0; i < dcover.size(); ++i)
       if (dcover[i] != 1) ++bad;
     if (bad) fail(std::string(what) + ": " + std::to_string(bad) + " output elements not written exactly once");
   }
 }
 
-void replay_norm(const NormArgs& g, int batch, bool scale, const char* what) {
+void replay_norm(const NormArgs& g, int batch, bool scale, int es, const char* what) {
   const int NT = 256;
-  for (int slice = 0; slice < batch; ++slice)
-    for (int chunk = 0; chunk < g.chunks; ++chunk) {
-      const long long v0 = (long long)chunk * g.chunk_vecs;
-      const long long v1 = (v0 + g.chunk_vecs < g.slice_vecs) ? v0 + g.chunk_vecs : g.slice_vecs;
-      if (v0 >= g.slice_vecs) fail(std::string(what) + ": empty norm block");
-      // first and last vector of each thread's strided walk
-      for (int tid = 0; tid < NT; ++tid) {
-        const long long first = v0 + tid;
-        if (first >= v1) continue;
-        const long long last = first + ((v1 - 1 - first) / NT) * NT;
-        for (long long v : {first, last}) {
-          access(g.x, ((long long)slice * g.slice_vecs + v) * 16, 16, what);
-          if (scale) access(g.y, ((long long)slice * g.slice_vecs + v) * 16, 16, what);
+  if (!scale) {
+    for (int slice = 0; slice < batch; ++slice)
+      for (int chunk = 0; chunk < g.chunks; ++chunk) {
+        const long long v0 = (long long)chunk * g.chunk_vecs;
+        const long long v1 = (v0 + g.chunk_vecs < g.slice_vecs) ? v0 + g.chunk_vecs : g.slice_vecs;
+        if (v0 >= g.slice_vecs) fail(std::string(what) + ": empty norm block");
+        for (int tid = 0; tid < NT; ++tid) {
+          const long long first = v0 + tid;
+          if (first >= v1) continue;
+          const long long last = first + ((v1 - 1 - first) / NT) * NT;
+          for (long long v : {first, last}) access(g.x, ((long long)slice * g.slice_vecs + v) * 16, 16, what);
         }
-      }
-      if (scale) {
-        for (int i = 0; i < g.chunks; ++i) access(g.partials, ((long long)slice * g.chunks + i) * 4, 4, what);
-        if (g.norms) access(g.norms, (long long)slice * 4, 4, what);
-      } else {
         access(g.partials, ((long long)slice * g.chunks + chunk) * 4, 4, what);
       }
+    return;
+  }
+  const int EPC = 16 / es, TS = kScaleTile, CPT = TS / EPC, SROW = TS + EPC;
+  const long long lds_bytes = (long long)TS * SROW * es;
+  std::vector<uint8_t> cov((size_t)g.rows * g.cols, 0), tcov(g.yt ? (size_t)g.rows * g.cols : 0, 0);
+  for (int slice = 0; slice < batch; ++slice)
+    for (int blk = 0; blk < g.tiles_r * g.tiles_c; ++blk) {
+      const int tr = blk / g.tiles_c, tc = blk % g.tiles_c;
+      for (int i = 0; i < g.chunks; ++i) access(g.partials, ((long long)slice * g.chunks + i) * 4, 4, what);
+      if (g.norms) access(g.norms, (long long)slice * 4, 4, what);
+      const long long base = (long long)slice * g.rows * g.cols;
+      for (int qd = 0; qd < TS * CPT; ++qd) {
+        const int r = qd / CPT, c = qd % CPT, gr = tr * TS + r, gc = tc * TS + c * EPC;
+        if (gr >= g.rows || gc >= g.cols) continue;
+        access(g.x, (base + (long long)gr * g.cols + gc) * es, 16, what);
+        access(g.y, (base + (long long)gr * g.cols + gc) * es, 16, what);
+        if (((long long)r * SROW + c * EPC) * es + 16 > lds_bytes) fail(std::string(what) + ": scale tile LDS");
+        if (slice == 0)
+          for (int e = 0; e < EPC; ++e) cov[(size_t)gr * g.cols + gc + e]++;
+      }
+      if (!g.yt) continue;
+      for (int qd = 0; qd < TS * CPT; ++qd) {
+        const int cl = qd % TS, rc = qd / TS, gc = tc * TS + cl, gr = tr * TS + rc * EPC;
+        if (gc >= g.cols || gr >= g.rows) continue;
+        if (((long long)(rc * EPC + EPC - 1) * SROW + cl) * es + es > lds_bytes) fail(std::string(what) + ": scale LDS");
+        access(g.yt, (base + (long long)gc * g.rows + gr) * es, 16, what);
+        if (slice == 0)
+          for (int e = 0; e < EPC; ++e) tcov[(size_t)gc * g.rows + gr + e]++;
+      }
+    }
+  for (size_t i = 0; i < cov.size(); ++i)
+    if (cov[i] != 1 || (!tcov.empty() && tcov[i] != 1)) {
+      fail(std::string(what) + ": scale output not covered exactly once");
+      break;
     }
 }
 
@@ -227,33 +291,38 @@ void replay_norm(const NormArgs& g, int batch, bool scale, const char* what) {
 void replay_call(int dtype, long long batch, long long rows, long long cols, int steps, bool alias) {
   g_bufs.clear();
   const Plan p = make_plan(batch, rows, cols, dtype);
-  const size_t xbytes = (size_t)batch * rows * cols * elem_size(dtype);
-  const size_t mm = (size_t)batch * p.m * p.m * elem_size(dtype);
+  const int es = (int)elem_size(dtype);
+  const size_t xbytes = (size_t)batch * rows * cols * es;
+  const size_t mm = (size_t)batch * p.m * p.m * es;
   void* in = reg(uintptr_t(1) << 44, "in", xbytes);
   void* out = alias ? in : reg(uintptr_t(2) << 44, "out", xbytes);
   void* xtmp = reg(uintptr_t(3) << 44, "xtmp", xbytes);
+  void* xt[2] = {reg(uintptr_t(9) << 44, "xt0", xbytes), reg(uintptr_t(10) << 44, "xt1", xbytes)};
   void* oa = reg(uintptr_t(4) << 44, "oa", mm);
   void* oc = reg(uintptr_t(5) << 44, "oc", mm);
   float* da = (float*)reg(uintptr_t(6) << 44, "da", (size_t)batch * p.m * 4);
   float* dc = (float*)reg(uintptr_t(7) << 44, "dc", (size_t)batch * p.m * 4);
   float* part = (float*)reg(uintptr_t(8) << 44, "partials", (size_t)batch * p.norm_chunks * 4);
   if (p.off_part + (size_t)batch * p.norm_chunks * 4 > p.total) fail("workspace plan too small");
+  if (p.off_xt1 - p.off_xt0 < xbytes || p.off_oa - p.off_xt1 < xbytes || p.off_xt0 - p.off_xtmp < xbytes)
+    fail("workspace plan overlaps the iterate buffers");
 
   auto buf = [&](int s) -> void* { return iterate_in_out(steps, s) ? out : xtmp; };
-  const NormArgs ng = norm_args(p, in, buf(0), nullptr, part);
-  replay_norm(ng, (int)batch, false, "sumsq");
-  replay_norm(ng, (int)batch, true, "scale");
+  const NormArgs ng = norm_args(p, in, buf(0), steps > 0 ? xt[0] : nullptr, nullptr, part);
+  replay_norm(ng, (int)batch, false, es, "sumsq");
+  replay_norm(ng, (int)batch, true, es, "scale");
   const bool cov = (long long)batch * std::max<long long>(p.m * p.m, rows * cols) <= 80LL * 1000 * 1000;
   for (int s = 1; s <= steps; ++s) {
     if (s != 1 && s != steps) continue;  // middle steps differ only in which buffer is which
-    StageKind k;
-    GemmArgs g = gram_args(p, buf(s - 1), oa, da, &k);
-    replay_gemm(g, k, dtype, cov, "gram");
-    g = poly_args(p, oa, da, oc, dc, 3.4445f, -4.775f, 2.0315f, &k);
-    replay_gemm(g, k, dtype, cov, "poly");
+    int mode;
+    GemmArgs g = gram_args(p, buf(s - 1), xt[(s - 1) & 1], oa, da, &mode);
+    replay_gemm(g, mode, dtype, plan_wide_tri(p), cov, "gram");
+    g = poly_args(p, oa, da, oc, dc, 3.4445f, -4.775f, 2.0315f, &mode);
+    replay_gemm(g, mode, dtype, plan_wide_tri(p), cov, "poly");
     if (buf(s - 1) == buf(s)) fail("update reads the buffer it writes");
-    g = update_args(p, buf(s - 1), oc, dc, buf(s), &k);
-    replay_gemm(g, k, dtype, cov, "update");
+    void* xto = (s < steps) ? xt[s & 1] : nullptr;
+    g = update_args(p, buf(s - 1), xt[(s - 1) & 1], oc, dc, buf(s), xto, &mode);
+    replay_gemm(g, mode, dtype, false, cov, "update");
   }
 }
 

@@ -8,8 +8,7 @@
 
 namespace ns {
 
-hipError_t launch_gemm(int dtype, int mode, int p_layout, int q_layout, const GemmArgs& g,
-                       hipStream_t st);
+hipError_t launch_gemm(int dtype, int mode, bool wide_tri, const GemmArgs& g, hipStream_t st);
 hipError_t launch_sumsq(int dtype, const NormArgs& g, int batch, hipStream_t st);
 hipError_t launch_scale(int dtype, const NormArgs& g, int batch, hipStream_t st);
 

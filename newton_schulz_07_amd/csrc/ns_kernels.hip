@@ -11,15 +11,14 @@
 // never pass through bf16 (the page credits fp32 epilogue arithmetic for the
 // symmetric path's accuracy; this placement extends that to the diagonals).
 //
-// Both operands of every product are staged in LDS as rows of K-contiguous
-// 16-byte chunks, so one inner loop serves all products:
-//   Gram, rows <= cols: P = Q = X rows              (K-contiguous in HBM)
-//   Gram, rows >  cols: P = Q = X columns           (transposed on load)
-//   poly:               P = Q = O_A rows            (A symmetric: A A = A Aᵀ)
-//   update, wide:       P = O_C rows, Q = X columns (transposed on load)
-//   update, tall:       P = X rows,   Q = O_C rows  (C symmetric)
-// Tall matrices are never transposed in HBM: their Gram side is the column
-// side, and X' = X C replaces the transpose-update-transpose.
+// The iterate is kept in HBM in both orientations, X and Xᵀ (the update
+// writes both from its staged output tile), so that every operand of every
+// product is read as K-contiguous rows:
+//   Gram, rows <= cols: P = Q = rows of X
+//   Gram, rows >  cols: P = Q = rows of Xᵀ
+//   poly:               P = Q = rows of O_A      (A symmetric: A A = A Aᵀ)
+//   update, wide:       P = rows of O_C, Q = rows of Xᵀ   (X' = C X)
+//   update, tall:       P = rows of X,   Q = rows of O_C  (X' = X C)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,20 +39,45 @@ template <> struct Elem<float> { static constexpr int kChunk = 4; };
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
-__device__ __forceinline__ uint4 ldg16(const void* p) {
-  return *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
-__device__ __forceinline__ float to_f32(float v) { return v; }
-template <typename T> __device__ __forceinline__ T from_f32(float v);
-template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
-template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (bf16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)hi) << 16);
+}
 
-// 16-byte chunk of operand values -> one MFMA step of the 32x32 block.
+// 4 consecutive elements of type T <-> 4 floats
+template <typename T> struct Quad;
+template <> struct Quad<bf16> {
+  typedef uint2 Raw;  // 8 bytes
+  __device__ __forceinline__ static void unpack(Raw r, float* f) {
+    f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x); f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
+  }
+  __device__ __forceinline__ static Raw pack(const float* f) {
+    return make_uint2(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]));
+  }
+};
+template <> struct Quad<float> {
+  typedef uint4 Raw;  // 16 bytes
+  __device__ __forceinline__ static void unpack(Raw r, float* f) {
+    f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y);
+    f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
+  }
+  __device__ __forceinline__ static Raw pack(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+};
+
+// 16-byte chunks of operand values -> one MFMA step of a 32x32 block.
 // bf16: the chunk is the 8-element k slice of v_mfma_f32_32x32x16_bf16.
-// fp32: the chunk is 4 k values, one per v_mfma_f32_32x32x2_f32; A and B use
-// the same k assignment, so the sum is the same product.
+// fp32: the chunk is 4 k values, one per v_mfma_f32_32x32x2_f32; both
+// operands use the same k assignment, so the sum is the same product.
 __device__ __forceinline__ void mfma_chunk(f32x16& acc, uint4 a, uint4 b, bf16) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
@@ -65,121 +89,70 @@ __device__ __forceinline__ void mfma_chunk(f32x16& acc, uint4 a, uint4 b, float)
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-// Transpose an EPC x EPC block held as EPC k-rows of 16 bytes (EPC values
-// along i) into EPC chunks of EPC values along k (one per i).
-__device__ __forceinline__ void transpose_block(const uint4* in, uint4* out, bf16) {
-  // dword d of k-row kk holds i = 2d (low half) and i = 2d+1 (high half).
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    uint32_t w[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) w[kk] = u4get(in[kk], d);
-    // v_perm_b32(hi, lo, sel): bytes 0-3 come from lo, 4-7 from hi.
-    out[2 * d] = make_uint4(__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
-                            __builtin_amdgcn_perm(w[3], w[2], 0x05040100u),
-                            __builtin_amdgcn_perm(w[5], w[4], 0x05040100u),
-                            __builtin_amdgcn_perm(w[7], w[6], 0x05040100u));
-    out[2 * d + 1] = make_uint4(__builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
-                                __builtin_amdgcn_perm(w[3], w[2], 0x07060302u),
-                                __builtin_amdgcn_perm(w[5], w[4], 0x07060302u),
-                                __builtin_amdgcn_perm(w[7], w[6], 0x07060302u));
-  }
-}
-__device__ __forceinline__ void transpose_block(const uint4* in, uint4* out, float) {
-#pragma unroll
-  for (int ii = 0; ii < 4; ++ii)
-    out[ii] = make_uint4(u4get(in[0], ii), u4get(in[1], ii), u4get(in[2], ii), u4get(in[3], ii));
-}
-
-// ----------------------------------------------------------------- loaders
-
-template <typename T, int LAYOUT, int R, int NT> struct OperandLoader;
-
-template <typename T, int R, int NT> struct OperandLoader<T, KCONT, R, NT> {
-  static constexpr int EPC = Elem<T>::kChunk;
-  static constexpr int NCH = R * 8;                   // chunks per stage
-  static constexpr int ITER = (NCH + NT - 1) / NT;
-  static constexpr int REGS = ITER;
-  __device__ __forceinline__ static void load(const T* base, int ld, int r0, int rmax, int k0,
-                                              int kmax, uint4* regs, int tid) {
-#pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int qd = tid + it * NT;
-      const KcontSrc s = kcont_src(qd);
-      const int gi = r0 + s.row, gk = k0 + s.ch * EPC;
-      const bool ok = (NCH % NT == 0 || qd < NCH) && gi < rmax && gk < kmax;
-      regs[it] = ok ? ldg16(base + (size_t)gi * ld + gk) : zero4();
-    }
-  }
-  __device__ __forceinline__ static void store(uint4* lds, const uint4* regs, int tid) {
-#pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int qd = tid + it * NT;
-      if (NCH % NT == 0 || qd < NCH) {
-        const KcontSrc s = kcont_src(qd);
-        lds[lds_swz(s.row, s.ch)] = regs[it];
-      }
-    }
-  }
-};
-
-template <typename T, int R, int NT> struct OperandLoader<T, MCONT, R, NT> {
-  static constexpr int EPC = Elem<T>::kChunk;
-  static constexpr int IB = R / EPC;                  // i-blocks per stage
-  static constexpr int NBLK = IB * 8;                 // 8 k-blocks (BK = 8 EPC)
-  static constexpr int ITER = (NBLK + NT - 1) / NT;
-  static constexpr int REGS = ITER * EPC;
-  __device__ __forceinline__ static void load(const T* base, int ld, int r0, int rmax, int k0,
-                                              int kmax, uint4* regs, int tid) {
-#pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int qd = tid + it * NT;
-      const McontSrc s = mcont_src(qd, IB);
-      const int gi = r0 + s.ib * EPC;
-      const bool blk = (NBLK % NT == 0 || qd < NBLK) && gi < rmax;
-#pragma unroll
-      for (int kk = 0; kk < EPC; ++kk) {
-        const int gk = k0 + s.kb * EPC + kk;
-        regs[it * EPC + kk] = (blk && gk < kmax) ? ldg16(base + (size_t)gk * ld + gi) : zero4();
-      }
-    }
-  }
-  __device__ __forceinline__ static void store(uint4* lds, const uint4* regs, int tid) {
-#pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int qd = tid + it * NT;
-      if (NBLK % NT == 0 || qd < NBLK) {
-        const McontSrc s = mcont_src(qd, IB);
-        uint4 t[EPC];
-        transpose_block(regs + it * EPC, t, T());
-#pragma unroll
-        for (int ii = 0; ii < EPC; ++ii) lds[lds_swz(s.ib * EPC + ii, s.kb)] = t[ii];
-      }
-    }
-  }
-};
-
 // ------------------------------------------------------------- MFMA kernel
 
-template <typename T, int BM, int BN, int WM, int WN, int PL, int QL, int MODE>
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor (gfx9 V#) over `bytes` bytes at `base`, stride 0: a load
+// at an offset >= bytes returns zeros.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  i32x4 r = {(int)(a & 0xffffffffu), (int)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+  return r;
+}
+
+// 16 bytes per lane from buffer offset voff into LDS at m0 + 16 * lane
+// (buffer_load_dwordx4 ... lds).  Issued through asm so that the compiler,
+// which cannot tell ring slots apart, does not wait for these loads before
+// every LDS read; the kernel waits for them explicitly (wait_vm_lgkm0).
+__device__ __forceinline__ void dma16(unsigned lds_byte_addr, unsigned voff, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_byte_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ unsigned lds_addr(const uint4* p) {
+  return (unsigned)reinterpret_cast<unsigned long long>((__attribute__((address_space(3))) const uint4*)p);
+}
+
+// s_waitcnt with vmcnt(N), lgkmcnt(0), expcnt unchanged (gfx9 encoding:
+// vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8, vmcnt[5:4] bits 15:14).
+template <int N> __device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier that also keeps the compiler from moving memory accesses
+// across it; the caller's explicit waits make the LDS data visible.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int CPR, int ST, int MODE>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
-  constexpr int NT = WM * WN * 64;
+  constexpr int NT = WM * WN * 64, NW = WM * WN;
   constexpr int EPC = Elem<T>::kChunk;
-  constexpr int BK = 8 * EPC;
+  constexpr int ES = (int)sizeof(T);
+  constexpr int BK = CPR * EPC;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int SM = WTM / 32, SN = WTN / 32;
+  constexpr int LP = BM * CPR, LQ = BN * CPR;  // chunks of each operand per stage
+  constexpr int STAGE = LP + LQ;
+  constexpr int NIW = STAGE / 64 / NW;         // load instructions per wave per stage
+  constexpr int ERC = epi_row_chunks(BN, ES);  // staged output row, in chunks
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(!mode_is_tri(MODE) || BM == BN, "triangle modes need square tiles");
-  using LP = OperandLoader<T, PL, BM, NT>;
-  using LQ = OperandLoader<T, QL, BN, NT>;
+  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "4, 8 or 16 chunks per LDS row");
+  static_assert(LP % 64 == 0 && STAGE % (64 * NW) == 0, "stage must split into whole wave loads");
+  static_assert(ST >= 2 && NIW * (ST - 2) < 64, "ring depth");
 
-  __shared__ uint4 lds[2][(BM + BN) * 8];
+  __shared__ uint4 lds[lds_chunks(BM, BN, CPR, ST, ES)];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -190,8 +163,36 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   else rect_decode(q, g.tiles_m, g.tiles_n, ti, tj);
   const int i0 = ti * BM, j0 = tj * BN;
 
-  const T* P = reinterpret_cast<const T*>(g.P) + (size_t)slice * g.p_bs;
-  const T* Q = reinterpret_cast<const T*>(g.Q) + (size_t)slice * g.q_bs;
+  // Buffer descriptors over the two operand slices: an offset at or past the
+  // slice end reads as zero, which fills rows past M / N and k past K.
+  const T* Pbase = reinterpret_cast<const T*>(g.P) + (size_t)slice * g.p_bs;
+  const T* Qbase = reinterpret_cast<const T*>(g.Q) + (size_t)slice * g.q_bs;
+  const i32x4 rP = make_rsrc(Pbase, (unsigned)(g.p_bs * ES));
+  const i32x4 rQ = make_rsrc(Qbase, (unsigned)(g.q_bs * ES));
+  constexpr unsigned kOutOfRange = 0x80000000u;
+
+  // per-lane source of each of this wave's load instructions (same every stage)
+  unsigned src_off[NIW];
+  int src_k[NIW];
+#pragma unroll
+  for (int t = 0; t < NIW; ++t) {
+    const DmaSrc d = dma_src(wave * NIW + t, lane, BM, CPR);
+    const int grow = (d.is_p ? i0 : j0) + d.row;
+    const bool rowok = grow < (d.is_p ? g.M : g.N);
+    const int ld = d.is_p ? g.ldp : g.ldq;
+    src_off[t] = rowok ? (unsigned)(((size_t)grow * ld + d.ch * EPC) * ES) : kOutOfRange;
+    src_k[t] = rowok ? d.ch * EPC : g.K;  // k offset of the chunk; >= K means zero
+  }
+  auto issue = [&](int kt, int slot) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int t = 0; t < NIW; ++t) {
+      const int idx = wave * NIW + t;  // wave-uniform
+      const unsigned off = (k0 + src_k[t] < g.K) ? src_off[t] + (unsigned)(k0 * ES) : kOutOfRange;
+      const unsigned dst = lds_addr(lds + slot * STAGE + idx * 64);
+      dma16(dst, off, idx * 64 < LP ? rP : rQ);
+    }
+  };
 
   f32x16 acc[SM][SN];
 #pragma unroll
@@ -201,88 +202,151 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  uint4 pr[LP::REGS], qr[LQ::REGS];
-  const int nk = (g.K + BK - 1) / BK;
-
-  LP::load(P, g.ldp, i0, g.M, 0, g.K, pr, tid);
-  LQ::load(Q, g.ldq, j0, g.N, 0, g.K, qr, tid);
-  LP::store(lds[0], pr, tid);
-  LQ::store(lds[0] + BM * 8, qr, tid);
-  __syncthreads();
-
   const int half = lane >> 5, l32 = lane & 31;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      LP::load(P, g.ldp, i0, g.M, (kt + 1) * BK, g.K, pr, tid);
-      LQ::load(Q, g.ldq, j0, g.N, (kt + 1) * BK, g.K, qr, tid);
-    }
-    const uint4* Ps = lds[cur];
-    const uint4* Qs = lds[cur] + BM * 8;
+  auto compute = [&](int slot) {
+    const uint4* Ps = lds + slot * STAGE;
+    const uint4* Qs = Ps + LP;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < CPR / 2; ++s) {
       const int ch = 2 * s + half;
-      uint4 af[SM], bq[SN];
+      uint4 pf[SM], qf[SN];
 #pragma unroll
-      for (int a = 0; a < SM; ++a) af[a] = Ps[lds_swz(wm * WTM + a * 32 + l32, ch)];
+      for (int a = 0; a < SM; ++a) pf[a] = Ps[lds_swz(wm * WTM + a * 32 + l32, ch, CPR)];
 #pragma unroll
-      for (int b = 0; b < SN; ++b) bq[b] = Qs[lds_swz(wn * WTN + b * 32 + l32, ch)];
+      for (int b = 0; b < SN; ++b) qf[b] = Qs[lds_swz(wn * WTN + b * 32 + l32, ch, CPR)];
 #pragma unroll
       for (int a = 0; a < SM; ++a)
 #pragma unroll
-        for (int b = 0; b < SN; ++b) mfma_chunk(acc[a][b], af[a], bq[b], T());
+        for (int b = 0; b < SN; ++b) mfma_chunk(acc[a][b], qf[b], pf[a], T());
     }
-    if (more) {
-      LP::store(lds[cur ^ 1], pr, tid);
-      LQ::store(lds[cur ^ 1] + BM * 8, qr, tid);
-    }
-    __syncthreads();
+  };
+
+  // Ring of ST stages: stage kt lives in slot kt % ST.  Before computing
+  // stage kt a wave waits until its own loads of stage kt are done (the
+  // loads of the up to ST-2 later stages may stay in flight); the barrier
+  // then publishes every wave's part, and also certifies that slot
+  // (kt-1) % ST is no longer read, so stage kt+ST-1 can be loaded into it.
+  const int nk = (g.K + BK - 1) / BK;
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int after = nk - 1 - kt;  // stages issued after kt, capped at ST-2
+    if (after >= ST - 2) wait_vm_lgkm0<NIW * (ST - 2)>();
+    else if (ST > 3 && after == 2) wait_vm_lgkm0<NIW * 2>();
+    else if (ST > 2 && after == 1) wait_vm_lgkm0<NIW>();
+    else wait_vm_lgkm0<0>();
+    ring_barrier();
+    if (kt + ST - 1 < nk) issue(kt + ST - 1, (kt + ST - 1) % ST);
+    compute(kt % ST);
   }
+  wait_vm_lgkm0<0>();
+  __syncthreads();
 
   // ------------------------------------------------------------ epilogue
+  // 1. fp32 epilogue in registers, converted values staged in LDS as the
+  //    BM x BN tile (rows padded by one chunk);
+  // 2. direct store of tile rows; 3. transposed store (mirror / Xᵀ).
   T* O = reinterpret_cast<T*>(g.out) + (size_t)slice * g.o_bs;
   const T* E = reinterpret_cast<const T*>(g.E) + (size_t)slice * g.e_bs;
   const float* din = g.d_in + (size_t)slice * g.d_bs;
   float* dout = g.d_out + (size_t)slice * g.d_bs;
   const bool diag_tile = mode_is_tri(MODE) && ti == tj;
+  T* S = reinterpret_cast<T*>(lds);
+  constexpr int SROW = ERC * EPC;  // staged row stride in elements
 
 #pragma unroll
-  for (int a = 0; a < SM; ++a)
+  for (int a = 0; a < SM; ++a) {
+    const int il = wm * WTM + a * 32 + acc_i(lane);
+    const int i = i0 + il;
 #pragma unroll
     for (int b = 0; b < SN; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i0 + wm * WTM + a * 32 + acc_row(r, lane);
-        const int col = j0 + wn * WTN + b * 32 + acc_col(lane);
-        if (row >= g.M || col >= g.N) continue;
-        const float v = acc[a][b][r];
-        if (MODE == MODE_GRAM || MODE == MODE_POLY) {
-          if (diag_tile && row < col) continue;  // written by the mirror
-          if (row == col) {
-            if (MODE == MODE_GRAM) {
-              dout[row] = v;
-            } else {
-              const float d = din[row];
-              dout[row] = g.ca + g.cb * d + g.cc * (v + d * d);
+      for (int rg = 0; rg < 4; ++rg) {
+        const int jl = wn * WTN + b * 32 + acc_j(rg, lane);
+        const int j = j0 + jl;
+        if (i >= g.M || j >= g.N) continue;  // N % 8 == 0: j..j+3 all valid
+        float v[4] = {acc[a][b][4 * rg], acc[a][b][4 * rg + 1], acc[a][b][4 * rg + 2], acc[a][b][4 * rg + 3]};
+        float w[4];
+        if (MODE == MODE_GRAM) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w[e] = v[e];
+            if (i == j + e) {
+              dout[i] = v[e];
+              w[e] = 0.0f;
             }
-            O[(size_t)row * g.ldo + col] = from_f32<T>(0.0f);
-          } else {
-            float w = v;
-            if (MODE == MODE_POLY) {
-              const float o = to_f32(E[(size_t)row * g.lde + col]);
-              w = g.cb * o + g.cc * (v + (din[row] + din[col]) * o);
+          }
+        } else if (MODE == MODE_POLY) {
+          float o[4];
+          Quad<T>::unpack(*reinterpret_cast<const typename Quad<T>::Raw*>(E + (size_t)i * g.lde + j), o);
+          const float4 dj = *reinterpret_cast<const float4*>(din + j);
+          const float dje[4] = {dj.x, dj.y, dj.z, dj.w};
+          const float di = din[i];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w[e] = g.cb * o[e] + g.cc * (v[e] + (di + dje[e]) * o[e]);
+            if (i == j + e) {
+              dout[i] = g.ca + g.cb * di + g.cc * (v[e] + di * di);
+              w[e] = 0.0f;
             }
-            const T t = from_f32<T>(w);
-            O[(size_t)row * g.ldo + col] = t;
-            O[(size_t)col * g.ldo + row] = t;
           }
         } else {
-          const float d = (MODE == MODE_UPD_ROW) ? din[row] : din[col];
-          const float x = to_f32(E[(size_t)row * g.lde + col]);
-          O[(size_t)row * g.ldo + col] = from_f32<T>(v + d * x);
+          float x[4];
+          Quad<T>::unpack(*reinterpret_cast<const typename Quad<T>::Raw*>(E + (size_t)i * g.lde + j), x);
+          if (MODE == MODE_UPD_ROW) {
+            const float di = din[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = v[e] + di * x[e];
+          } else {
+            const float4 dj = *reinterpret_cast<const float4*>(din + j);
+            w[0] = v[0] + dj.x * x[0];
+            w[1] = v[1] + dj.y * x[1];
+            w[2] = v[2] + dj.z * x[2];
+            w[3] = v[3] + dj.w * x[3];
+          }
         }
+        *reinterpret_cast<typename Quad<T>::Raw*>(S + il * SROW + jl) = Quad<T>::pack(w);
       }
+  }
+  __syncthreads();
+
+  // 2. direct store: chunk (il, c) = elements il, [8c/4c .. +EPC) of the tile
+  constexpr int CPT = BN / EPC;  // chunks per tile row
+  for (int qd = tid; qd < BM * CPT; qd += NT) {
+    const int il = qd / CPT, c = qd % CPT;
+    const int i = i0 + il, j = j0 + c * EPC;
+    if (i >= g.M || j >= g.N) continue;
+    uint4 val;
+    if (diag_tile && c * EPC + EPC - 1 > il) {
+      // upper part of a diagonal tile: take the mirror of the lower part
+      T tmp[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const int jl = c * EPC + e;
+        tmp[e] = (jl <= il) ? S[il * SROW + jl] : S[jl * SROW + il];
+      }
+      val = *reinterpret_cast<const uint4*>(tmp);
+    } else {
+      val = *reinterpret_cast<const uint4*>(S + il * SROW + c * EPC);
+    }
+    *reinterpret_cast<uint4*>(O + (size_t)i * g.ldo + j) = val;
+  }
+
+  // 3. transposed store: column jl of the tile, rows [EPC r .. +EPC)
+  if (g.out_t != nullptr && !diag_tile) {
+    T* OT = reinterpret_cast<T*>(g.out_t) + (size_t)slice * g.ot_bs;
+    constexpr int RCH = BM / EPC;  // chunks per transposed row
+    for (int qd = tid; qd < BN * RCH; qd += NT) {
+      const int jl = qd % BN, rc = qd / BN;
+      const int j = j0 + jl, i = i0 + rc * EPC;
+      if (j >= g.N || i >= g.M) continue;
+      T tmp[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) tmp[e] = S[(rc * EPC + e) * SROW + jl];
+      *reinterpret_cast<uint4*>(OT + (size_t)j * g.ldt + i) = *reinterpret_cast<const uint4*>(tmp);
+    }
+  }
 }
 
 // --------------------------------------------------------- normalisation
@@ -298,7 +362,7 @@ __device__ __forceinline__ float sumsq16(uint4 u, bf16) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const uint32_t w = u4get(u, d);
-    const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+    const float lo = bf16_lo(w), hi = bf16_hi(w);
     s = fmaf(lo, lo, s);
     s = fmaf(hi, hi, s);
   }
@@ -319,9 +383,7 @@ __device__ __forceinline__ uint4 scale16(uint4 u, float inv, bf16) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const uint32_t w = u4get(u, d);
-    const bf16 lo = (bf16)(__uint_as_float(w << 16) * inv);
-    const bf16 hi = (bf16)(__uint_as_float(w & 0xffff0000u) * inv);
-    o[d] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    o[d] = pack_bf16(bf16_lo(w) * inv, bf16_hi(w) * inv);
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
@@ -354,11 +416,19 @@ __global__ __launch_bounds__(kNormThreads) void sumsq_kernel(const NormArgs g) {
 }
 
 // Pass 2: every block sums its slice's partials (same order in every block),
-// then writes x / (sqrt(sum) + eps) in the storage dtype.
+// then scales one 64 x 64 tile: X0 = x / (sqrt(sum) + eps) written row-wise,
+// and (if yt is set) X0ᵀ written through an LDS transpose.
 template <typename T>
 __global__ __launch_bounds__(kNormThreads) void scale_kernel(const NormArgs g) {
+  constexpr int EPC = Elem<T>::kChunk;
+  constexpr int TS = kScaleTile;
+  constexpr int CPT = TS / EPC;           // chunks per tile row
+  constexpr int SROW = TS + EPC;          // padded LDS row, elements
   __shared__ float s_inv;
-  const int slice = blockIdx.y, chunk = blockIdx.x;
+  __shared__ uint4 tile_raw[TS * SROW / EPC];
+  T* tile = reinterpret_cast<T*>(tile_raw);
+  const int slice = blockIdx.y;
+  const int tr = blockIdx.x / g.tiles_c, tc = blockIdx.x % g.tiles_c;
   if (threadIdx.x < 64) {
     float s = 0.0f;
     for (int i = threadIdx.x; i < g.chunks; i += 64) s += g.partials[(size_t)slice * g.chunks + i];
@@ -366,48 +436,62 @@ __global__ __launch_bounds__(kNormThreads) void scale_kernel(const NormArgs g) {
     if (threadIdx.x == 0) {
       const float nrm = sqrtf(s);
       s_inv = 1.0f / (nrm + g.eps);
-      if (g.norms != nullptr && chunk == 0) g.norms[slice] = nrm;
+      if (g.norms != nullptr && blockIdx.x == 0) g.norms[slice] = nrm;
     }
   }
   __syncthreads();
   const float inv = s_inv;
-  const uint4* xv = reinterpret_cast<const uint4*>(g.x) + (size_t)slice * g.slice_vecs;
-  uint4* yv = reinterpret_cast<uint4*>(g.y) + (size_t)slice * g.slice_vecs;
-  const long long v0 = (long long)chunk * g.chunk_vecs;
-  const long long v1 = (v0 + g.chunk_vecs < g.slice_vecs) ? v0 + g.chunk_vecs : g.slice_vecs;
-  for (long long v = v0 + threadIdx.x; v < v1; v += kNormThreads) yv[v] = scale16(xv[v], inv, T());
+  const size_t base = (size_t)slice * g.rows * g.cols;
+  const T* x = reinterpret_cast<const T*>(g.x) + base;
+  T* y = reinterpret_cast<T*>(g.y) + base;
+  for (int qd = threadIdx.x; qd < TS * CPT; qd += kNormThreads) {
+    const int r = qd / CPT, c = qd % CPT;
+    const int gr = tr * TS + r, gc = tc * TS + c * EPC;
+    if (gr >= g.rows || gc >= g.cols) continue;
+    const uint4 v = scale16(ldg16(x + (size_t)gr * g.cols + gc), inv, T());
+    *reinterpret_cast<uint4*>(y + (size_t)gr * g.cols + gc) = v;
+    *reinterpret_cast<uint4*>(tile + r * SROW + c * EPC) = v;
+  }
+  if (g.yt == nullptr) return;  // uniform across the block
+  __syncthreads();
+  T* yt = reinterpret_cast<T*>(g.yt) + base;
+  for (int qd = threadIdx.x; qd < TS * CPT; qd += kNormThreads) {
+    const int cl = qd % TS, rc = qd / TS;  // tile column cl, rows [EPC rc, +EPC)
+    const int gc = tc * TS + cl, gr = tr * TS + rc * EPC;
+    if (gc >= g.cols || gr >= g.rows) continue;
+    T tmp[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) tmp[e] = tile[(rc * EPC + e) * SROW + cl];
+    *reinterpret_cast<uint4*>(yt + (size_t)gc * g.rows + gr) = *reinterpret_cast<const uint4*>(tmp);
+  }
 }
 
 // ------------------------------------------------------------- launchers
 
-template <typename T, int BM, int BN, int WM, int WN, int PL, int QL, int MODE>
-static hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t st) {
+template <typename T, int MODE, bool WIDE>
+static hipError_t launch_mode(const GemmArgs& g, hipStream_t st) {
+  constexpr TileCfg t = tile_cfg(std::is_same<T, bf16>::value ? 1 : 0, mode_is_tri(MODE), WIDE);
   const int total = g.tiles_per_slice * g.batch;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, PL, QL, MODE>), dim3(total), dim3(WM * WN * 64),
-                     0, st, g);
+  hipLaunchKernelGGL((gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.cpr, t.st, MODE>), dim3(total),
+                     dim3(t.wm * t.wn * 64), 0, st, g);
   return hipGetLastError();
 }
 
-template <typename T, int PL, int QL, int MODE>
-static hipError_t dispatch_tile(const GemmArgs& g, hipStream_t st) {
-  constexpr TileCfg t = std::is_same<T, bf16>::value ? kTileBf16 : kTileF32;
-  return launch_gemm_t<T, t.bm, t.bn, t.wm, t.wn, PL, QL, MODE>(g, st);
-}
-
 template <typename T>
-static hipError_t dispatch_mode(int mode, int pl, int ql, const GemmArgs& g, hipStream_t st) {
-  if (mode == MODE_GRAM && pl == KCONT) return dispatch_tile<T, KCONT, KCONT, MODE_GRAM>(g, st);
-  if (mode == MODE_GRAM && pl == MCONT) return dispatch_tile<T, MCONT, MCONT, MODE_GRAM>(g, st);
-  if (mode == MODE_POLY) return dispatch_tile<T, KCONT, KCONT, MODE_POLY>(g, st);
-  if (mode == MODE_UPD_ROW) return dispatch_tile<T, KCONT, MCONT, MODE_UPD_ROW>(g, st);
-  if (mode == MODE_UPD_COL) return dispatch_tile<T, KCONT, KCONT, MODE_UPD_COL>(g, st);
-  return hipErrorInvalidValue;
+static hipError_t dispatch_mode(int mode, bool wide_tri, const GemmArgs& g, hipStream_t st) {
+  const bool wide = wide_tri && std::is_same<T, bf16>::value;
+  switch (mode) {
+    case MODE_GRAM: return wide ? launch_mode<T, MODE_GRAM, true>(g, st) : launch_mode<T, MODE_GRAM, false>(g, st);
+    case MODE_POLY: return wide ? launch_mode<T, MODE_POLY, true>(g, st) : launch_mode<T, MODE_POLY, false>(g, st);
+    case MODE_UPD_ROW: return launch_mode<T, MODE_UPD_ROW, false>(g, st);
+    case MODE_UPD_COL: return launch_mode<T, MODE_UPD_COL, false>(g, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
-hipError_t launch_gemm(int dtype, int mode, int p_layout, int q_layout, const GemmArgs& g,
-                       hipStream_t st) {
-  if (dtype == 1) return dispatch_mode<bf16>(mode, p_layout, q_layout, g, st);
-  return dispatch_mode<float>(mode, p_layout, q_layout, g, st);
+hipError_t launch_gemm(int dtype, int mode, bool wide_tri, const GemmArgs& g, hipStream_t st) {
+  if (dtype == 1) return dispatch_mode<bf16>(mode, wide_tri, g, st);
+  return dispatch_mode<float>(mode, wide_tri, g, st);
 }
 
 hipError_t launch_sumsq(int dtype, const NormArgs& g, int batch, hipStream_t st) {
@@ -418,7 +502,7 @@ hipError_t launch_sumsq(int dtype, const NormArgs& g, int batch, hipStream_t st)
 }
 
 hipError_t launch_scale(int dtype, const NormArgs& g, int batch, hipStream_t st) {
-  dim3 grid(g.chunks, batch);
+  dim3 grid(g.tiles_r * g.tiles_c, batch);
   if (dtype == 1) hipLaunchKernelGGL(scale_kernel<bf16>, grid, dim3(kNormThreads), 0, st, g);
   else hipLaunchKernelGGL(scale_kernel<float>, grid, dim3(kNormThreads), 0, st, g);
   return hipGetLastError();

@@ -26,11 +26,57 @@ enum GemmMode : int {
 
 NS_HD constexpr bool mode_is_tri(int mode) { return mode == MODE_GRAM || mode == MODE_POLY; }
 
-// How an operand tile is read from global memory.
-enum OperandLayout : int {
-  KCONT = 0,  // element (i, k) at base + i * ld + k   (k contiguous)
-  MCONT = 1   // element (i, k) at base + k * ld + i   (i contiguous)
+// Tile shape of one kernel instance: BM x BN output tile, WM x WN waves of
+// 64 lanes, CPR 16-byte chunks per LDS row (K stage = CPR * 16 bytes of each
+// operand row), ST = K stages held in the LDS ring (loads run ST-1 stages
+// ahead of the MFMAs).
+struct TileCfg {
+  int bm, bn, wm, wn, cpr, st;
 };
+
+#ifndef NS_TILE_BF16_TRI
+#define NS_TILE_BF16_TRI {128, 128, 2, 4, 8, 2}
+#endif
+#ifndef NS_TILE_BF16_TRI_WIDE
+#define NS_TILE_BF16_TRI_WIDE {192, 192, 2, 2, 8, 2}
+#endif
+#ifndef NS_TILE_BF16_RECT
+#define NS_TILE_BF16_RECT {256, 256, 2, 4, 8, 2}
+#endif
+#ifndef NS_TILE_F32_TRI
+#define NS_TILE_F32_TRI {128, 128, 2, 2, 8, 3}
+#endif
+#ifndef NS_TILE_F32_RECT
+#define NS_TILE_F32_RECT {128, 128, 2, 2, 8, 3}
+#endif
+constexpr TileCfg kTileBf16Tri = NS_TILE_BF16_TRI;
+constexpr TileCfg kTileBf16TriWide = NS_TILE_BF16_TRI_WIDE;
+constexpr TileCfg kTileBf16Rect = NS_TILE_BF16_RECT;
+constexpr TileCfg kTileF32Tri = NS_TILE_F32_TRI;
+constexpr TileCfg kTileF32Rect = NS_TILE_F32_RECT;
+
+// Triangle kernels (Gram, poly) have two bf16 tile shapes: 128 x 128 with
+// two workgroups per CU, and 192 x 192 with one.  A stack with few lower
+// triangle tiles (fewer than two rounds of 512 workgroup slots at 128) would
+// leave a nearly empty last round, so it takes the larger tile instead
+// (m = 4096: 528 tiles at 128, 253 tiles at 192 on 256 CUs).
+NS_HD constexpr bool use_wide_tri(int dtype, long long batch, long long m) {
+  return dtype == 1 && batch * ((m + 127) / 128) * ((m + 127) / 128 + 1) / 2 < 1024;
+}
+NS_HD constexpr TileCfg tile_cfg(int dtype, bool tri, bool wide_tri = false) {
+  return dtype == 1 ? (tri ? (wide_tri ? kTileBf16TriWide : kTileBf16Tri) : kTileBf16Rect)
+                    : (tri ? kTileF32Tri : kTileF32Rect);
+}
+NS_HD constexpr int elems_per_chunk(int dtype) { return dtype == 1 ? 8 : 4; }
+
+// LDS of one kernel instance, in 16-byte chunks: the ring of ST K stages of
+// both operands, or the epilogue's staged output tile (rows padded by one
+// chunk), whichever is larger.
+NS_HD constexpr int epi_row_chunks(int bn, int esize) { return bn * esize / 16 + 1; }
+NS_HD constexpr int lds_chunks(int bm, int bn, int cpr, int st, int esize) {
+  return st * (bm + bn) * cpr > bm * epi_row_chunks(bn, esize) ? st * (bm + bn) * cpr
+                                                               : bm * epi_row_chunks(bn, esize);
+}
 
 // The hardware hands workgroup w to XCD (w mod 8).  Remap so that each XCD
 // works through one contiguous range of logical tile ids (neighbouring tiles
@@ -64,44 +110,60 @@ NS_HD void rect_decode(int q, int tiles_m, int tiles_n, int& ti, int& tj) {
   tj = r / gs;
 }
 
-// LDS tile: rows of 8 chunks of 16 bytes.  The chunk position is XOR-swizzled
-// with row bits 0-2 and 3-5 so that (a) 16 lanes reading the same logical
-// chunk of 16 consecutive rows and (b) 8 lanes writing the same chunk of rows
-// 8 apart both hit distinct bank groups.
-NS_HD int lds_swz(int row, int ch) { return row * 8 + (ch ^ ((row ^ (row >> 3)) & 7)); }
+// K-stage operand tile in LDS: rows of CPR (4, 8 or 16) chunks of 16 bytes.
+// Chunk ch of a row is stored at position ch ^ f(row) with
+// f(row) = (row ^ (row >> log2 CPR)) & (CPR - 1), so that the 8 or 16 lanes
+// that the LDS serves together, reading one logical chunk of consecutive
+// rows, hit distinct bank groups.  XOR is its own inverse: the loader puts
+// the global chunk phys ^ f(row) at position phys.
+NS_HD int swz_f(int row, int cpr) {
+  const int sh = cpr == 4 ? 2 : cpr == 8 ? 3 : 4;
+  return (row ^ (row >> sh)) & (cpr - 1);
+}
+NS_HD int lds_swz(int row, int ch, int cpr) { return row * cpr + (ch ^ swz_f(row, cpr)); }
 
-// K-contiguous loader: chunk qd of an R x (8 chunks) stage.
-struct KcontSrc {
-  int row, ch;  // position in the tile
+// Loader: each wave instruction fills 64 consecutive chunks of a stage (one
+// 16-byte chunk per lane).  Instruction idx of a stage covers chunk positions
+// [64 idx, 64 idx + 64): the P rows first, then the Q rows.
+struct DmaSrc {
+  bool is_p;     // operand P (else Q)
+  int row;       // row of the operand tile
+  int ch;        // logical chunk (k offset ch * 16 bytes) loaded by this lane
+  int lds_pos;   // chunk position in the stage slot written by this lane
 };
-NS_HD KcontSrc kcont_src(int qd) { return KcontSrc{qd >> 3, qd & 7}; }
+NS_HD DmaSrc dma_src(int idx, int lane, int bm, int cpr) {
+  const int p = idx * 64 + lane;
+  const bool is_p = p < bm * cpr;
+  const int pp = is_p ? p : p - bm * cpr;
+  const int row = pp / cpr, phys = pp % cpr;
+  return DmaSrc{is_p, row, phys ^ swz_f(row, cpr), p};
+}
 
-// M-contiguous loader: block qd of (R/EPC) x 8 blocks; each block is EPC
-// k-rows by EPC consecutive i (one 16-byte load per k-row).
-struct McontSrc {
-  int ib, kb;  // block coordinates: rows ib*EPC.., k-chunk kb
-};
-NS_HD McontSrc mcont_src(int qd, int iblocks) { return McontSrc{qd % iblocks, qd / iblocks}; }
+// MFMA operand roles: the A operand is the Q tile (output column j), the B
+// operand the P tile (output row i).  Register r of lane l of a 32x32 block
+// then holds row i = l % 32 and column j = 8 (r / 4) + 4 (l / 32) + r % 4,
+// so each group of 4 registers is 4 consecutive columns of one row.
+NS_HD int acc_i(int lane) { return lane & 31; }
+NS_HD int acc_j(int rgroup, int lane) { return 8 * rgroup + 4 * (lane >> 5); }
 
-// Accumulator layout of v_mfma_f32_32x32x*: register r of lane l holds
-// row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the 32x32 block.
-NS_HD int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-NS_HD int acc_col(int lane) { return lane & 31; }
-
-// Arguments of one tiled MFMA launch over `batch` slices.
-// The kernel computes acc(i, j) = sum_k P(i, k) Q(j, k) over an M x N output,
-// reduction length K, then applies the mode's epilogue (ns_layout.h).
+// Arguments of one tiled MFMA launch over `batch` slices.  The kernel forms
+// acc(i, j) = sum_k P(i, k) Q(j, k) over an M x N output with reduction
+// length K (both operands K-contiguous), applies the mode's epilogue, stores
+// the tile to `out` and, if out_t is set, its transpose to out_t.
 struct GemmArgs {
-  const void* P;      // operand P, slice 0
-  const void* Q;      // operand Q, slice 0
+  const void* P;      // operand P rows, slice 0
+  const void* Q;      // operand Q rows, slice 0
   long long p_bs;     // slice strides, in elements
   long long q_bs;
   int ldp, ldq;       // leading dimensions, in elements
   int M, N, K;
   int tiles_m, tiles_n, tiles_per_slice, batch;
-  void* out;          // output matrix (m x m for Gram/poly, X' for update)
+  void* out;          // output (m x m for Gram/poly, X' for update)
   long long o_bs;
   int ldo;
+  void* out_t;        // transposed output (mirror for Gram/poly, X'ᵀ), or null
+  long long ot_bs;
+  int ldt;
   const void* E;      // epilogue matrix: O_A (poly) or X (update); unused for Gram
   long long e_bs;
   int lde;
@@ -111,27 +173,22 @@ struct GemmArgs {
   float ca, cb, cc;   // quintic coefficients (poly only)
 };
 
-// Arguments of the two normalisation passes.
+// Normalisation: per-slice sum of squares over 32 KiB blocks, then a 2-D
+// tiled scale pass that writes X0 and X0ᵀ.
+constexpr int kScaleTile = 64;   // scale pass: 64 x 64 element tiles
+
 struct NormArgs {
-  const void* x;       // input  [batch, elems]
-  void* y;             // output [batch, elems] (scale pass), may equal x
-  float* partials;     // [batch, chunks] sums of squares
-  float* norms;        // optional [batch] Frobenius norms (scale pass)
+  const void* x;         // input  [batch, rows, cols]
+  void* y;               // X0 [batch, rows, cols] (scale pass), may equal x
+  void* yt;              // X0ᵀ [batch, cols, rows] (scale pass), or null
+  float* partials;       // [batch, chunks] sums of squares
+  float* norms;          // optional [batch] Frobenius norms (scale pass)
   long long slice_vecs;  // 16-byte vectors per slice
-  long long chunk_vecs;  // 16-byte vectors per block
-  int chunks;          // blocks per slice
+  long long chunk_vecs;  // 16-byte vectors per sum-of-squares block
+  int chunks;            // sum-of-squares blocks per slice
+  int rows, cols;
+  int tiles_r, tiles_c;  // scale-pass tiles per slice
   float eps;
 };
-
-// Tile shape of the MFMA kernel per storage dtype: BM x BN output tile,
-// WM x WN waves (64 lanes each); the K stage is 8 chunks of 16 bytes
-// (64 bf16 or 32 fp32 values).
-struct TileCfg {
-  int bm, bn, wm, wn;
-};
-constexpr TileCfg kTileBf16 = {128, 128, 2, 2};
-constexpr TileCfg kTileF32 = {128, 128, 2, 2};
-NS_HD constexpr TileCfg tile_cfg(int dtype) { return dtype == 1 ? kTileBf16 : kTileF32; }
-NS_HD constexpr int elems_per_chunk(int dtype) { return dtype == 1 ? 8 : 4; }
 
 }  // namespace ns

@@ -25,7 +25,7 @@ struct Plan {
   int dtype;
   int norm_chunks;
   // workspace offsets (bytes)
-  size_t off_xtmp, off_oa, off_oc, off_da, off_dc, off_part, total;
+  size_t off_xtmp, off_xt0, off_xt1, off_oa, off_oc, off_da, off_dc, off_part, total;
 };
 
 inline Plan make_plan(int64_t batch, int64_t rows, int64_t cols, int dtype) {
@@ -40,9 +40,14 @@ inline Plan make_plan(int64_t batch, int64_t rows, int64_t cols, int dtype) {
   const size_t es = elem_size(dtype);
   const long long vecs = rows * cols * (long long)es / 16;
   p.norm_chunks = (int)((vecs + kNormChunkVecs - 1) / kNormChunkVecs);
+  const size_t xbytes = ws_align((size_t)batch * rows * cols * es);
   size_t off = 0;
   p.off_xtmp = off;
-  off += ws_align((size_t)batch * rows * cols * es);
+  off += xbytes;
+  p.off_xt0 = off;
+  off += xbytes;
+  p.off_xt1 = off;
+  off += xbytes;
   p.off_oa = off;
   off += ws_align((size_t)batch * p.m * p.m * es);
   p.off_oc = off;
@@ -59,53 +64,56 @@ inline Plan make_plan(int64_t batch, int64_t rows, int64_t cols, int dtype) {
 
 // The iterate X_s (s = 0 after normalisation) is held in `out` when
 // (steps - s) is even and in the workspace temporary otherwise, so the last
-// step writes `out` and no update reads the buffer it writes.
+// step writes `out` and no update reads the buffer it writes.  Its transpose
+// X_sᵀ alternates between two workspace buffers (xt0 for even s).
 inline bool iterate_in_out(int steps, int s) { return ((steps - s) % 2) == 0; }
 
-inline NormArgs norm_args(const Plan& p, const void* x, void* y, float* norms, float* partials) {
+inline NormArgs norm_args(const Plan& p, const void* x, void* y, void* yt, float* norms, float* partials) {
   NormArgs g{};
   g.x = x;
   g.y = y;
+  g.yt = yt;
   g.partials = partials;
   g.norms = norms;
   g.slice_vecs = p.rows * p.cols * (long long)elem_size(p.dtype) / 16;
   g.chunk_vecs = kNormChunkVecs;
   g.chunks = p.norm_chunks;
+  g.rows = (int)p.rows;
+  g.cols = (int)p.cols;
+  g.tiles_r = tiles_of(p.rows, kScaleTile);
+  g.tiles_c = tiles_of(p.cols, kScaleTile);
   g.eps = kNormEps;
   return g;
 }
 
-// Which operand loaders a stage uses.
-struct StageKind {
-  int mode, p_layout, q_layout;
-};
+// A = X Xᵀ (rows <= cols: rows of X) or Xᵀ X (rows > cols: rows of Xᵀ),
+// mirrored into the same m x m matrix.
+inline bool plan_wide_tri(const Plan& p) { return use_wide_tri(p.dtype, p.batch, p.m); }
 
-// A = X Xᵀ (rows <= cols: rows of X) or Xᵀ X (rows > cols: columns of X).
-inline GemmArgs gram_args(const Plan& p, const void* x, void* oa, float* da, StageKind* kind) {
-  const TileCfg t = tile_cfg(p.dtype);
+inline GemmArgs gram_args(const Plan& p, const void* x, const void* xt, void* oa, float* da, int* mode) {
+  const TileCfg t = tile_cfg(p.dtype, true, plan_wide_tri(p));
   GemmArgs g{};
-  g.P = g.Q = x;
+  g.P = g.Q = p.tall ? xt : x;
   g.p_bs = g.q_bs = p.rows * p.cols;
-  g.ldp = g.ldq = (int)p.cols;
+  g.ldp = g.ldq = (int)p.n;
   g.M = g.N = (int)p.m;
   g.K = (int)p.n;
   g.tiles_m = g.tiles_n = tiles_of(p.m, t.bm);
   g.tiles_per_slice = g.tiles_m * (g.tiles_m + 1) / 2;
   g.batch = (int)p.batch;
-  g.out = oa;
-  g.o_bs = p.m * p.m;
-  g.ldo = (int)p.m;
+  g.out = g.out_t = oa;
+  g.o_bs = g.ot_bs = p.m * p.m;
+  g.ldo = g.ldt = (int)p.m;
   g.d_out = da;
   g.d_bs = p.m;
-  const int layout = p.tall ? MCONT : KCONT;
-  *kind = StageKind{MODE_GRAM, layout, layout};
+  *mode = MODE_GRAM;
   return g;
 }
 
 // C = a I + b A + c A A from the split A, written split the same way.
 inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* oc, float* dc, float a,
-                          float b, float c, StageKind* kind) {
-  const TileCfg t = tile_cfg(p.dtype);
+                          float b, float c, int* mode) {
+  const TileCfg t = tile_cfg(p.dtype, true, plan_wide_tri(p));
   GemmArgs g{};
   g.P = g.Q = oa;
   g.p_bs = g.q_bs = p.m * p.m;
@@ -114,9 +122,9 @@ inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* 
   g.tiles_m = g.tiles_n = tiles_of(p.m, t.bm);
   g.tiles_per_slice = g.tiles_m * (g.tiles_m + 1) / 2;
   g.batch = (int)p.batch;
-  g.out = oc;
-  g.o_bs = p.m * p.m;
-  g.ldo = (int)p.m;
+  g.out = g.out_t = oc;
+  g.o_bs = g.ot_bs = p.m * p.m;
+  g.ldo = g.ldt = (int)p.m;
   g.E = oa;
   g.e_bs = p.m * p.m;
   g.lde = (int)p.m;
@@ -126,23 +134,24 @@ inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* 
   g.ca = a;
   g.cb = b;
   g.cc = c;
-  *kind = StageKind{MODE_POLY, KCONT, KCONT};
+  *mode = MODE_POLY;
   return g;
 }
 
-// X' = C X (rows <= cols) or X C (rows > cols), C = O_C + diag(d_C).
-inline GemmArgs update_args(const Plan& p, const void* x, const void* oc, const float* dc, void* xo,
-                            StageKind* kind) {
-  const TileCfg t = tile_cfg(p.dtype);
+// X' = C X (rows <= cols) or X C (rows > cols), C = O_C + diag(d_C); writes
+// X' and, when xto is set, X'ᵀ.
+inline GemmArgs update_args(const Plan& p, const void* x, const void* xt, const void* oc, const float* dc,
+                            void* xo, void* xto, int* mode) {
+  const TileCfg t = tile_cfg(p.dtype, false);
   GemmArgs g{};
-  if (!p.tall) {  // P = rows of O_C, Q = columns of X
+  if (!p.tall) {  // P = rows of O_C, Q = rows of Xᵀ (columns of X)
     g.P = oc;
     g.p_bs = p.m * p.m;
     g.ldp = (int)p.m;
-    g.Q = x;
+    g.Q = xt;
     g.q_bs = p.rows * p.cols;
-    g.ldq = (int)p.cols;
-    *kind = StageKind{MODE_UPD_ROW, KCONT, MCONT};
+    g.ldq = (int)p.rows;
+    *mode = MODE_UPD_ROW;
   } else {  // P = rows of X, Q = rows of O_C (C is symmetric)
     g.P = x;
     g.p_bs = p.rows * p.cols;
@@ -150,7 +159,7 @@ inline GemmArgs update_args(const Plan& p, const void* x, const void* oc, const 
     g.Q = oc;
     g.q_bs = p.m * p.m;
     g.ldq = (int)p.m;
-    *kind = StageKind{MODE_UPD_COL, KCONT, KCONT};
+    *mode = MODE_UPD_COL;
   }
   g.M = (int)p.rows;
   g.N = (int)p.cols;
@@ -162,6 +171,9 @@ inline GemmArgs update_args(const Plan& p, const void* x, const void* oc, const 
   g.out = xo;
   g.o_bs = p.rows * p.cols;
   g.ldo = (int)p.cols;
+  g.out_t = xto;
+  g.ot_bs = p.rows * p.cols;
+  g.ldt = (int)p.rows;
   g.E = x;
   g.e_bs = p.rows * p.cols;
   g.lde = (int)p.cols;

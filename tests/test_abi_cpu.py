@@ -46,6 +46,7 @@ def call(batch=1, rows=256, cols=512, dtype=1, steps=5, inp=FAKE_IN, out=FAKE_OU
     (dict(batch=-1), 1),
     (dict(steps=-1), 1),
     (dict(rows=65536, cols=65536), 1),     # slice of 2^32 elements
+    (dict(rows=16384, cols=32768), 1),     # 2^29 elements: over the 2 GiB fp32 slice limit
     (dict(dtype=2), 2),
     (dict(dtype=-1), 2),
     (dict(rows=260), 3),                   # not a multiple of 8
@@ -68,20 +69,25 @@ def test_empty_batch_is_a_no_op():
 def test_stage_argument_errors():
     L = ns.lib()
     vp = ctypes.c_void_p
-    assert L.ns_stage_gram(vp(FAKE_IN), vp(0), vp(FAKE_OUT), 1, 64, 64, 1, None) == 1
+    big = FAKE_OUT + (1 << 24)
+    assert L.ns_stage_gram(vp(FAKE_IN), None, vp(0), vp(FAKE_OUT), 1, 64, 64, 1, None) == 1
+    assert L.ns_stage_gram(vp(FAKE_IN), None, vp(FAKE_OUT), vp(big), 1, 128, 64, 1, None) == 1  # tall needs xt
     assert L.ns_stage_poly(vp(FAKE_IN), vp(FAKE_OUT), vp(FAKE_IN), vp(FAKE_OUT), 1, 64, 1, 1.0, 0.0, 0.0, None) == 1
-    assert L.ns_stage_update(vp(FAKE_IN), vp(FAKE_OUT), vp(FAKE_OUT + 1 << 20), vp(FAKE_IN), 1, 64, 64, 1, None) == 1
-    assert L.ns_stage_normalize(vp(FAKE_IN), vp(FAKE_OUT), None, 1, 63, 64, 1, None) == 3
-    assert L.ns_stage_normalize(vp(FAKE_IN), vp(FAKE_OUT), None, 0, 64, 64, 1, None) == 0
+    assert L.ns_stage_update(vp(FAKE_IN), None, vp(FAKE_OUT), vp(big), vp(big * 2), None, 1, 64, 64, 1, None) == 1
+    assert L.ns_stage_update(vp(FAKE_IN), vp(big), vp(FAKE_OUT), vp(big * 2), vp(FAKE_IN), None,
+                             1, 64, 64, 1, None) == 1  # x_out overlaps x
+    assert L.ns_stage_normalize(vp(FAKE_IN), vp(FAKE_OUT), None, None, 1, 63, 64, 1, None) == 3
+    assert L.ns_stage_normalize(vp(FAKE_IN), vp(FAKE_OUT), None, None, 0, 64, 64, 1, None) == 0
 
 
 def test_workspace_bytes():
     L = ns.lib()
-    # temporary X + two m x m matrices + two fp32 diagonals + norm partials
+    # temporary X + two copies of Xᵀ + two m x m matrices + two fp32 diagonals
+    # + norm partials
     b, r, c = 128, 1536, 2048
     ws = L.ns_workspace_bytes(b, r, c, 1)
-    assert ws >= b * r * c * 2 + 2 * b * r * r * 2 + 2 * b * r * 4
-    assert ws < 1.01 * (b * r * c * 2 + 2 * b * r * r * 2) + (1 << 20)
+    assert ws >= 3 * b * r * c * 2 + 2 * b * r * r * 2 + 2 * b * r * 4
+    assert ws < 1.01 * (3 * b * r * c * 2 + 2 * b * r * r * 2) + (1 << 20)
     assert L.ns_workspace_bytes(1, 14336, 4096, 1) == L.ns_workspace_bytes(1, 4096, 14336, 1)
     assert L.ns_workspace_bytes(1, 10, 16, 1) == 0  # invalid shape
     assert L.ns_workspace_bytes(1, 16, 16, 7) == 0  # invalid dtype

@@ -1,0 +1,94 @@
+"""Full-size parity: every named workload at its real shape, in the launch
+configuration the benchmark times (the whole stack in one call), against the
+fp64 oracle on sampled slices (the oracle computes slices one by one).
+
+Bars (relative Frobenius error per slice):
+  * bf16 path: <= 1e-2.  Two workloads cannot meet it with ANY bf16 iterate:
+    on the rank-64-plus-noise square and the rank-32-plus-noise MLP weight the
+    low-rank part dominates every entry, so rounding X to bf16 perturbs the
+    noise subspace by about the noise itself, and NS amplifies small singular
+    values (about a^5 ≈ 485).  The CPU rounding model
+    (tests/golden/rounding_floor.json) puts their floor above 1e-2.  For those
+    the bar is 1.25 x that floor, and a strict xfail records the 1e-2 miss.
+  * fp32 path on the same inputs: <= 1e-3 (fp32 vs fp64 NS differ by a few
+    1e-4 at these sizes), which checks every tile of the kernels at full size.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import newton_schulz_07_amd as ns
+from ns_inputs import WORKLOADS, make_workload
+from oracle import newton_schulz
+from tests.gpu_util import device, rel_err, report, to64
+
+pytestmark = pytest.mark.gpu
+
+FLOOR = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "rounding_floor.json")))["workloads"]
+SAMPLES = {"experts16_1536x2048": [0, 7, 15], "experts128_1536x2048": [0, 63, 127],
+           "experts32_7168x2048": [0, 31]}
+FLOORED = {"lowrank64_4096x4096", "mlp_4096x14336", "mlp_14336x4096"}
+
+_oracle_cache = {}
+
+
+def oracle_slice(name, x, i):
+    key = (name, i)
+    if key not in _oracle_cache:
+        if name == "mlp_14336x4096" and ("mlp_4096x14336", i) in _oracle_cache:
+            _oracle_cache[key] = _oracle_cache[("mlp_4096x14336", i)].T
+        else:
+            _oracle_cache[key] = newton_schulz(x.double().numpy())
+    return _oracle_cache[key]
+
+
+def run(name, dtype):
+    w = WORKLOADS[name]
+    x = make_workload(name)
+    xg = x.to(dtype).to(device())
+    y = ns.orthogonalize(xg)
+    torch.cuda.synchronize()
+    xs = x.reshape(-1, w.rows, w.cols)
+    ys = y.reshape(-1, w.rows, w.cols)
+    errs = {}
+    for i in SAMPLES.get(name, [0]):
+        ref = oracle_slice(name, xs[i], i)
+        errs[i] = float(rel_err(to64(ys[i]), ref)[0])
+    assert torch.isfinite(y).all()
+    return errs
+
+
+NAMES = ["lowrank64_4096x4096", "mlp_4096x14336", "mlp_14336x4096", "experts16_1536x2048",
+         "experts128_1536x2048", "experts32_7168x2048", "square_8192x8192"]
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_full_size_bf16(name):
+    errs = run(name, torch.bfloat16)
+    floors = {int(k): v["diag"] for k, v in FLOOR[name].items()}
+    report({"case": f"full_bf16_{name}", "errs": errs, "model_floor": floors})
+    for i, e in errs.items():
+        if name in FLOORED:
+            assert e <= 1.25 * floors[i], (i, e, floors[i])
+        else:
+            assert e <= 1e-2, (i, e)
+
+
+@pytest.mark.parametrize("name", sorted(FLOORED))
+@pytest.mark.xfail(strict=True, reason="inherent bf16-iterate floor above 1e-2 on this input "
+                                       "(see tests/golden/rounding_floor.json)")
+def test_full_size_bf16_meets_1e_2_on_floored_inputs(name):
+    errs = run(name, torch.bfloat16)
+    assert max(errs.values()) <= 1e-2
+
+
+@pytest.mark.parametrize("name", ["lowrank64_4096x4096", "mlp_14336x4096", "experts16_1536x2048",
+                                  "experts32_7168x2048"])
+def test_full_size_fp32(name):
+    errs = run(name, torch.float32)
+    report({"case": f"full_fp32_{name}", "errs": errs})
+    assert max(errs.values()) <= 1e-3

@@ -135,7 +135,7 @@ def test_config_query_names_the_kernels():
     dev = device()
     ns.orthogonalize(gaussian((2, 64, 128), 750, torch.bfloat16).to(dev))
     cfg = ns.ns_query_last_config()
-    assert "mfma=32x32x16_bf16" in cfg and "gram=lower-tri" in cfg and "batch=2" in cfg
+    assert "mfma=32x32x16_bf16" in cfg and "gram,poly: lower-tri" in cfg and "batch=2" in cfg
 
 
 def test_timing_records_each_launch():
