@@ -138,24 +138,18 @@ int ns_timing_query(int kind, double* total_ms, int64_t* launches);
 
 /* ---- single stages (the same kernels ns_orthogonalize runs) ------------- */
 /* Shapes: a slice of x is rows x cols; m = min(rows, cols).  The Gram side is
- * the short one: A = X Xᵀ when rows <= cols, A = Xᵀ X when rows > cols.
- * Inside ns_orthogonalize the iterate is kept as X and as Xᵀ ([batch, cols,
- * rows], row-major), so every product reads K-contiguous rows; the stage
- * entry points take and produce that transposed copy explicitly. */
+ * the short one: A = X Xᵀ when rows <= cols, A = Xᵀ X when rows > cols. */
 
 /* X0 = x / (||x||_F + 1e-7) per slice, same shape, layout and dtype.
- * x0t (optional, may be NULL) receives X0ᵀ [batch, cols, rows].
  * norms (optional, may be NULL): fp32 [batch] receives ||x||_F per slice.
- * x0 may equal x; x0t must overlap neither. */
-int ns_stage_normalize(const void* x, void* x0, void* x0t, float* norms, int64_t batch,
+ * x0 may equal x. */
+int ns_stage_normalize(const void* x, void* x0, float* norms, int64_t batch,
                        int64_t rows, int64_t cols, int dtype, void* stream);
 
-/* Gram of each slice.  Reads x when rows <= cols, xt = xᵀ [batch, cols,
- * rows] when rows > cols (the other pointer is not read and may be NULL).
- * a_off [batch, m, m] (dtype) receives the off-diagonal entries with exact
- * zeros on the diagonal and is bitwise symmetric; a_diag fp32 [batch, m]
- * receives the diagonal. */
-int ns_stage_gram(const void* x, const void* xt, void* a_off, float* a_diag, int64_t batch,
+/* Gram of each slice: a_off [batch, m, m] (dtype) receives the off-diagonal
+ * entries with exact zeros on the diagonal and is bitwise symmetric;
+ * a_diag fp32 [batch, m] receives the diagonal. */
+int ns_stage_gram(const void* x, void* a_off, float* a_diag, int64_t batch,
                   int64_t rows, int64_t cols, int dtype, void* stream);
 
 /* C = a I + b A + c A A from A = a_off + diag(a_diag), stored the same way:
@@ -166,12 +160,11 @@ int ns_stage_poly(const void* a_off, const float* a_diag, void* c_off,
                   float b, float c, void* stream);
 
 /* One update with C = c_off + diag(c_diag):
- *   rows <= cols:  x_out = C x   (reads x and xt = xᵀ)
- *   rows >  cols:  x_out = x C   (reads x; xt is not read and may be NULL)
- * xt_out (optional, may be NULL) receives x_outᵀ [batch, cols, rows].
- * Outputs must not overlap inputs or each other. */
-int ns_stage_update(const void* x, const void* xt, const void* c_off, const float* c_diag,
-                    void* x_out, void* xt_out, int64_t batch, int64_t rows, int64_t cols,
+ *   rows <= cols:  x_out = C x         (C is rows x rows)
+ *   rows >  cols:  x_out = x C         (C is cols x cols)
+ * x_out must not overlap x. */
+int ns_stage_update(const void* x, const void* c_off, const float* c_diag,
+                    void* x_out, int64_t batch, int64_t rows, int64_t cols,
                     int dtype, void* stream);
 
 #ifdef __cplusplus

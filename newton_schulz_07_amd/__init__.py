@@ -35,10 +35,10 @@ SIGNATURES = {
     "ns_timing_enable": (_int, [_int]),
     "ns_timing_reset": (_int, []),
     "ns_timing_query": (_int, [_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
-    "ns_stage_normalize": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]),
-    "ns_stage_gram": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]),
+    "ns_stage_normalize": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]),
+    "ns_stage_gram": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]),
     "ns_stage_poly": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _flt, _flt, _flt, _vp]),
-    "ns_stage_update": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]),
+    "ns_stage_update": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]),
 }
 
 _lib = None
@@ -161,39 +161,28 @@ def ns_timing_query(kind):
 
 # ------------------------------------------------------------------ stages
 
-def _transposed_like(x):
-    import torch
-    return torch.empty(x.shape[:-2] + (x.shape[-1], x.shape[-2]), dtype=x.dtype, device=x.device)
-
-
-def ns_stage_normalize(x, x0=None, norms=None, with_transpose=False):
-    """X0 (and X0ᵀ if with_transpose): returns x0 or (x0, x0t)."""
+def ns_stage_normalize(x, x0=None, norms=None):
+    """X0 = x / (||x||_F + 1e-7) per slice."""
     import torch
     _need_gpu_tensor(x, "x")
     x0 = torch.empty_like(x) if x0 is None else x0
-    x0t = _transposed_like(x) if with_transpose else None
     batch, rows, cols = _brc(x)
     with torch.cuda.device(x.device):
-        _check(lib().ns_stage_normalize(_ptr(x), _ptr(x0), _ptr(x0t), _ptr(norms), batch, rows, cols,
+        _check(lib().ns_stage_normalize(_ptr(x), _ptr(x0), _ptr(norms), batch, rows, cols,
                                         _dtype_code(x), _stream(x)))
-    return (x0, x0t) if with_transpose else x0
+    return x0
 
 
-def ns_stage_gram(x, xt=None):
-    """Returns (a_off [batch, m, m] in x's dtype, a_diag fp32 [batch, m]).
-    A tall x (rows > cols) is read through xt = xᵀ, which the caller supplies."""
+def ns_stage_gram(x):
+    """Returns (a_off [batch, m, m] in x's dtype, a_diag fp32 [batch, m])."""
     import torch
     _need_gpu_tensor(x, "x")
     batch, rows, cols = _brc(x)
-    if rows > cols:
-        if xt is None:
-            raise ValueError("a tall x needs its transpose xt")
-        _need_gpu_tensor(xt, "xt")
     m = min(rows, cols)
     a_off = torch.empty((batch, m, m), dtype=x.dtype, device=x.device)
     a_diag = torch.empty((batch, m), dtype=torch.float32, device=x.device)
     with torch.cuda.device(x.device):
-        _check(lib().ns_stage_gram(_ptr(x), _ptr(xt), _ptr(a_off), _ptr(a_diag), batch, rows, cols,
+        _check(lib().ns_stage_gram(_ptr(x), _ptr(a_off), _ptr(a_diag), batch, rows, cols,
                                    _dtype_code(x), _stream(x)))
     return a_off, a_diag
 
@@ -214,24 +203,18 @@ def ns_stage_poly(a_off, a_diag, a=DEFAULT_COEFFS[0], b=DEFAULT_COEFFS[1], c=DEF
     return c_off, c_diag
 
 
-def ns_stage_update(x, c_off, c_diag, xt=None, with_transpose=False):
-    """x_out = C x (rows <= cols; needs xt = xᵀ) or x C (rows > cols).
-    Returns x_out, or (x_out, x_outᵀ) if with_transpose."""
+def ns_stage_update(x, c_off, c_diag):
+    """x_out = C x (rows <= cols) or x C (rows > cols), C = c_off + diag(c_diag)."""
     import torch
     _need_gpu_tensor(x, "x")
     _need_gpu_tensor(c_off, "c_off")
     _need_gpu_tensor(c_diag, "c_diag")
     batch, rows, cols = _brc(x)
-    if rows <= cols:
-        if xt is None:
-            raise ValueError("a wide x needs its transpose xt")
-        _need_gpu_tensor(xt, "xt")
     m = min(rows, cols)
     if c_off.numel() != batch * m * m or c_diag.numel() != batch * m or c_diag.dtype != torch.float32:
         raise ValueError("c_off must be [batch, m, m] and c_diag fp32 [batch, m], m = min(rows, cols)")
     x_out = torch.empty_like(x)
-    xt_out = _transposed_like(x) if with_transpose else None
     with torch.cuda.device(x.device):
-        _check(lib().ns_stage_update(_ptr(x), _ptr(xt), _ptr(c_off), _ptr(c_diag), _ptr(x_out), _ptr(xt_out),
-                                     batch, rows, cols, _dtype_code(x), _stream(x)))
-    return (x_out, xt_out) if with_transpose else x_out
+        _check(lib().ns_stage_update(_ptr(x), _ptr(c_off), _ptr(c_diag), _ptr(x_out), batch, rows, cols,
+                                     _dtype_code(x), _stream(x)))
+    return x_out

@@ -166,9 +166,8 @@ hipError_t timed_launch(int kind, hipStream_t st, F&& f) {
 
 // ---------------------------------------------------------------- stages
 
-int run_normalize(const void* x, void* y, void* yt, float* norms, const Plan& p, float* partials,
-                  hipStream_t st) {
-  const NormArgs g = ns::norm_args(p, x, y, yt, norms, partials);
+int run_normalize(const void* x, void* y, float* norms, const Plan& p, float* partials, hipStream_t st) {
+  const NormArgs g = ns::norm_args(p, x, y, norms, partials);
   const int batch = (int)p.batch;
   if (int s = check_hip(timed_launch(NS_KIND_SUMSQ, st, [&] { return ns::launch_sumsq(p.dtype, g, batch, st); }),
                         "sum-of-squares launch"))
@@ -177,43 +176,42 @@ int run_normalize(const void* x, void* y, void* yt, float* norms, const Plan& p,
                    "scale launch");
 }
 
-int launch_stage(int kind_id, const char* what, const Plan& p, const GemmArgs& g, int mode, hipStream_t st) {
-  const bool wide_tri = ns::plan_wide_tri(p);
-  return check_hip(timed_launch(kind_id, st, [&] { return ns::launch_gemm(p.dtype, mode, wide_tri, g, st); }), what);
+int launch_stage(int kind_id, const char* what, const Plan& p, const GemmArgs& g, const ns::StageKind& k,
+                 hipStream_t st) {
+  return check_hip(timed_launch(kind_id, st, [&] { return ns::launch_gemm(p.dtype, k, g, st); }), what);
 }
 
-int run_gram(const void* x, const void* xt, void* oa, float* da, const Plan& p, hipStream_t st) {
-  int mode;
-  const GemmArgs g = ns::gram_args(p, x, xt, oa, da, &mode);
-  return launch_stage(NS_KIND_GRAM, "gram launch", p, g, mode, st);
+int run_gram(const void* x, void* oa, float* da, const Plan& p, hipStream_t st) {
+  ns::StageKind k;
+  const GemmArgs g = ns::gram_args(p, x, oa, da, &k);
+  return launch_stage(NS_KIND_GRAM, "gram launch", p, g, k, st);
 }
 
 int run_poly(const void* oa, const float* da, void* oc, float* dc, const Plan& p, float a, float b,
              float c, hipStream_t st) {
-  int mode;
-  const GemmArgs g = ns::poly_args(p, oa, da, oc, dc, a, b, c, &mode);
-  return launch_stage(NS_KIND_POLY, "poly launch", p, g, mode, st);
+  ns::StageKind k;
+  const GemmArgs g = ns::poly_args(p, oa, da, oc, dc, a, b, c, &k);
+  return launch_stage(NS_KIND_POLY, "poly launch", p, g, k, st);
 }
 
-int run_update(const void* x, const void* xt, const void* oc, const float* dc, void* xo, void* xto,
-               const Plan& p, hipStream_t st) {
-  int mode;
-  const GemmArgs g = ns::update_args(p, x, xt, oc, dc, xo, xto, &mode);
-  return launch_stage(NS_KIND_UPDATE, "update launch", p, g, mode, st);
+int run_update(const void* x, const void* oc, const float* dc, void* xo, const Plan& p, hipStream_t st) {
+  ns::StageKind k;
+  const GemmArgs g = ns::update_args(p, x, oc, dc, xo, &k);
+  return launch_stage(NS_KIND_UPDATE, "update launch", p, g, k, st);
 }
 
 void record_config(const Plan& p, int steps) {
   const ns::TileCfg tt = ns::tile_cfg(p.dtype, true, ns::plan_wide_tri(p)), tr = ns::tile_cfg(p.dtype, false);
   char buf[640];
   std::snprintf(buf, sizeof(buf),
-                "dtype=%s batch=%lld rows=%lld cols=%lld m=%lld %s steps=%d | norm: sumsq(%lldx16B)+scale(%dx%d, X and "
-                "X^T) | mfma=%s | gram,poly: lower-tri tile=%dx%d waves=%dx%d k=%dB ring=%d | update: %s tile=%dx%d "
-                "waves=%dx%d k=%dB ring=%d",
+                "dtype=%s batch=%lld rows=%lld cols=%lld m=%lld %s steps=%d | norm: sumsq+scale (%lldx16B blocks) | "
+                "mfma=%s | gram,poly: lower-tri tile=%dx%d waves=%dx%d k=%dB ring=%d gram-operands=%s | update: %s "
+                "tile=%dx%d waves=%dx%d k=%dB ring=%d X-operand=%s",
                 p.dtype == NS_DTYPE_BF16 ? "bf16" : "fp32", (long long)p.batch, (long long)p.rows,
                 (long long)p.cols, (long long)p.m, p.tall ? "tall" : "wide", steps, ns::kNormChunkVecs,
-                ns::kScaleTile, ns::kScaleTile, p.dtype == NS_DTYPE_BF16 ? "32x32x16_bf16" : "32x32x2_f32", tt.bm,
-                tt.bn, tt.wm, tt.wn, tt.cpr * 16, tt.st, p.tall ? "X*C" : "C*X", tr.bm, tr.bn, tr.wm, tr.wn,
-                tr.cpr * 16, tr.st);
+                p.dtype == NS_DTYPE_BF16 ? "32x32x16_bf16" : "32x32x2_f32", tt.bm, tt.bn, tt.wm, tt.wn,
+                tt.cpr * 16, tt.st, p.tall ? "columns(transposed-read)" : "rows", p.tall ? "X*C" : "C*X", tr.bm,
+                tr.bn, tr.wm, tr.wn, tr.cpr * 16, tr.st, p.tall ? "rows" : "columns(transposed-read)");
   t_cfg = buf;
 }
 
@@ -252,7 +250,6 @@ int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows, int
   char* ws = nullptr;
   if (int s = get_workspace(st, p.total, &ws)) return s;
   void* xtmp = ws + p.off_xtmp;
-  void* xt[2] = {ws + p.off_xt0, ws + p.off_xt1};
   void* oa = ws + p.off_oa;
   void* oc = ws + p.off_oc;
   float* da = reinterpret_cast<float*>(ws + p.off_da);
@@ -261,12 +258,11 @@ int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows, int
 
   auto buf = [&](int s) -> void* { return ns::iterate_in_out(ns_steps, s) ? out : xtmp; };
 
-  if (int s = run_normalize(in, buf(0), ns_steps > 0 ? xt[0] : nullptr, nullptr, p, part, st)) return s;
+  if (int s = run_normalize(in, buf(0), nullptr, p, part, st)) return s;
   for (int s = 1; s <= ns_steps; ++s) {
-    if (int e = run_gram(buf(s - 1), xt[(s - 1) & 1], oa, da, p, st)) return e;
+    if (int e = run_gram(buf(s - 1), oa, da, p, st)) return e;
     if (int e = run_poly(oa, da, oc, dc, p, a, b, c, st)) return e;
-    void* xto = (s < ns_steps) ? xt[s & 1] : nullptr;  // the last step needs no transpose
-    if (int e = run_update(buf(s - 1), xt[(s - 1) & 1], oc, dc, buf(s), xto, p, st)) return e;
+    if (int e = run_update(buf(s - 1), oc, dc, buf(s), p, st)) return e;
   }
   record_config(p, ns_steps);
   return NS_OK;
@@ -354,38 +350,34 @@ int ns_timing_query(int kind, double* total_ms, int64_t* launches) {
   return NS_OK;
 }
 
-int ns_stage_normalize(const void* x, void* x0, void* x0t, float* norms, int64_t batch, int64_t rows,
-                       int64_t cols, int dtype, void* stream) {
+int ns_stage_normalize(const void* x, void* x0, float* norms, int64_t batch, int64_t rows, int64_t cols,
+                       int dtype, void* stream) {
   t_err.clear();
   if (int s = common_checks(batch, rows, cols, dtype)) return s;
   if (int s = check_ptr(x, "x")) return s;
   if (int s = check_ptr(x0, "x0")) return s;
-  if (x0t != nullptr)
-    if (int s = check_ptr(x0t, "x0t")) return s;
   const size_t bytes = (size_t)batch * rows * cols * esize(dtype);
   if (x != x0 && overlaps(x, bytes, x0, bytes)) return fail(NS_ERR_INVALID_ARG, "x0 overlaps x");
-  if (x0t != nullptr && (overlaps(x, bytes, x0t, bytes) || overlaps(x0, bytes, x0t, bytes)))
-    return fail(NS_ERR_INVALID_ARG, "x0t overlaps x or x0");
   if (batch == 0) return NS_OK;
   if (int s = check_arch()) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Plan p = make_plan(batch, rows, cols, dtype);
   char* ws = nullptr;
   if (int s = get_workspace(st, p.total, &ws)) return s;
-  return run_normalize(x, x0, x0t, norms, p, reinterpret_cast<float*>(ws + p.off_part), st);
+  return run_normalize(x, x0, norms, p, reinterpret_cast<float*>(ws + p.off_part), st);
 }
 
-int ns_stage_gram(const void* x, const void* xt, void* a_off, float* a_diag, int64_t batch, int64_t rows,
-                  int64_t cols, int dtype, void* stream) {
+int ns_stage_gram(const void* x, void* a_off, float* a_diag, int64_t batch, int64_t rows, int64_t cols,
+                  int dtype, void* stream) {
   t_err.clear();
   if (int s = common_checks(batch, rows, cols, dtype)) return s;
-  if (int s = check_ptr(rows > cols ? xt : x, rows > cols ? "xt" : "x")) return s;
+  if (int s = check_ptr(x, "x")) return s;
   if (int s = check_ptr(a_off, "a_off")) return s;
   if (int s = check_ptr(a_diag, "a_diag")) return s;
   if (batch == 0) return NS_OK;
   if (int s = check_arch()) return s;
   const Plan p = make_plan(batch, rows, cols, dtype);
-  return run_gram(x, xt, a_off, a_diag, p, static_cast<hipStream_t>(stream));
+  return run_gram(x, a_off, a_diag, p, static_cast<hipStream_t>(stream));
 }
 
 int ns_stage_poly(const void* a_off, const float* a_diag, void* c_off, float* c_diag, int64_t batch, int64_t m,
@@ -404,31 +396,20 @@ int ns_stage_poly(const void* a_off, const float* a_diag, void* c_off, float* c_
   return run_poly(a_off, a_diag, c_off, c_diag, p, a, b, c, static_cast<hipStream_t>(stream));
 }
 
-int ns_stage_update(const void* x, const void* xt, const void* c_off, const float* c_diag, void* x_out,
-                    void* xt_out, int64_t batch, int64_t rows, int64_t cols, int dtype, void* stream) {
+int ns_stage_update(const void* x, const void* c_off, const float* c_diag, void* x_out, int64_t batch,
+                    int64_t rows, int64_t cols, int dtype, void* stream) {
   t_err.clear();
   if (int s = common_checks(batch, rows, cols, dtype)) return s;
   if (int s = check_ptr(x, "x")) return s;
-  if (rows <= cols)
-    if (int s = check_ptr(xt, "xt")) return s;
   if (int s = check_ptr(c_off, "c_off")) return s;
   if (int s = check_ptr(c_diag, "c_diag")) return s;
   if (int s = check_ptr(x_out, "x_out")) return s;
-  if (xt_out != nullptr)
-    if (int s = check_ptr(xt_out, "xt_out")) return s;
   const size_t bytes = (size_t)batch * rows * cols * esize(dtype);
-  const void* ins[2] = {x, rows <= cols ? xt : nullptr};
-  void* outs[2] = {x_out, xt_out};
-  for (const void* i : ins)
-    for (void* o : outs)
-      if (i != nullptr && o != nullptr && overlaps(i, bytes, o, bytes))
-        return fail(NS_ERR_INVALID_ARG, "an output overlaps an input");
-  if (xt_out != nullptr && overlaps(x_out, bytes, xt_out, bytes))
-    return fail(NS_ERR_INVALID_ARG, "xt_out overlaps x_out");
+  if (overlaps(x, bytes, x_out, bytes)) return fail(NS_ERR_INVALID_ARG, "x_out overlaps x");
   if (batch == 0) return NS_OK;
   if (int s = check_arch()) return s;
   const Plan p = make_plan(batch, rows, cols, dtype);
-  return run_update(x, xt, c_off, c_diag, x_out, xt_out, p, static_cast<hipStream_t>(stream));
+  return run_update(x, c_off, c_diag, x_out, p, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -68,25 +68,27 @@ void lds_index(int idx, int limit, const char* what) {
 // every lane either reads 16 in-range bytes of its operand slice or uses an
 // offset at or past the slice end (which the buffer range check turns into
 // zeros); every LDS write lands inside the stage slot.
-void replay_dma(int wave, int niw, int bm, int cpr, int es, int k0, int K, const GemmArgs& g, int slice, int i0,
-                int j0, int stage_chunks, int slot, int lds_limit, const char* what) {
+void replay_dma(int wave, int niw, const TileCfg& t, int es, bool pnat, bool qnat, int k0, const GemmArgs& g,
+                int slice, int i0, int j0, int stage_chunks, int slot, int lds_limit, const char* what) {
   const int EPC = 16 / es;
   const unsigned kOut = 0x80000000u;
   const long long pbytes = g.p_bs * es, qbytes = g.q_bs * es;
   if (pbytes >= (long long)kOut || qbytes >= (long long)kOut) fail(std::string(what) + ": slice too large for the range trick");
-  for (int t = 0; t < niw; ++t) {
-    const int idx = wave * niw + t;
+  for (int ti = 0; ti < niw; ++ti) {
+    const int idx = wave * niw + ti;
     for (int lane = 0; lane < 64; ++lane) {
-      const DmaSrc d = dma_src(idx, lane, bm, cpr);
-      if ((idx * 64 < bm * cpr) != d.is_p) fail(std::string(what) + ": load instruction spans both operands");
+      const DmaSrc d = dma_src(idx, lane, t.bm, t.bn, t.cpr, EPC, pnat, qnat, es);
+      if ((idx * 64 < t.bm * t.cpr) != d.is_p) fail(std::string(what) + ": load instruction spans both operands");
       lds_index(slot * stage_chunks + idx * 64 + lane, lds_limit, what);
       if (idx * 64 + lane >= stage_chunks) fail(std::string(what) + ": load outside its stage slot");
-      const int grow = (d.is_p ? i0 : j0) + d.row;
-      const bool rowok = grow < (d.is_p ? g.M : g.N);
+      const bool nat = d.is_p ? pnat : qnat;
       const int ld = d.is_p ? g.ldp : g.ldq;
-      const bool ok = rowok && k0 + d.ch * EPC < K;
+      const int g_row = (d.is_p ? i0 : j0) + d.row;
+      const bool ok = g_row < (d.is_p ? g.M : g.N) && k0 + d.kpos < g.K;
+      if (d.row < 0 || d.row >= (d.is_p ? t.bm : t.bn) || d.kpos < 0 || d.kpos >= t.cpr * EPC)
+        fail(std::string(what) + ": loader index outside the tile");
       if (!ok) continue;  // offset kOut: reads zeros
-      const long long off = ((long long)grow * ld + d.ch * EPC + k0) * es;
+      const long long off = nat ? ((long long)(k0 + d.kpos) * ld + g_row) * es : ((long long)g_row * ld + k0 + d.kpos) * es;
       if (off + 16 > (d.is_p ? pbytes : qbytes) || off >= (long long)kOut)
         fail(std::string(what) + ": in-range load past the slice");
       access(d.is_p ? g.P : g.Q, (long long)slice * (d.is_p ? g.p_bs : g.q_bs) * es + off, 16, what);
@@ -94,10 +96,45 @@ void replay_dma(int wave, int niw, int bm, int cpr, int es, int k0, int K, const
   }
 }
 
+// Fragment reads of one operand region (mirrors compute()/nat_frag): every
+// LDS byte read lies inside the region.
+void replay_frag_reads(const TileCfg& t, int es, bool nat, int rows_region, int wave_rows, int nblk, int wofs,
+                       const char* what) {
+  const int EPC = 16 / es, rc = rows_region / EPC, region = rows_region * t.cpr;
+  for (int lane = 0; lane < 64; ++lane)
+    for (int s = 0; s < t.cpr / 2; ++s)
+      for (int a = 0; a < nblk; ++a) {
+        const int rb = wofs + a * 32;
+        if (!nat) {
+          lds_index(lds_swz(rb + (lane & 31), 2 * s + (lane >> 5), t.cpr), region, what);
+          continue;
+        }
+        if (es == 2) {
+          for (int h = 0; h < 2; ++h) {
+            const int kr = nat_tr_kr(s, h, lane), col = nat_tr_col(rb, lane);
+            if (kr >= t.cpr * EPC || col + 3 >= rows_region) fail(std::string(what) + ": transposed read outside tile");
+            const int c = (col >> 3) ^ nat_swz(kr, rc, es);
+            if (c >= rc) fail(std::string(what) + ": swizzled chunk past the row");
+            lds_index(kr * rc + c, region, what);
+          }
+        } else {
+          const int col = rb + (lane & 31);
+          for (int e = 0; e < 4; ++e) {
+            const int kr = 8 * s + 4 * (lane >> 5) + e;
+            const int c = (col >> 2) ^ nat_swz(kr, rc, es);
+            if (kr >= t.cpr * EPC || c >= rc) fail(std::string(what) + ": fp32 natural read outside tile");
+            lds_index(kr * rc + c, region, what);
+          }
+        }
+      }
+  (void)wave_rows;
+}
+
 // Replays one launch of gemm_kernel (grid = tiles_per_slice * batch).
-void replay_gemm(const GemmArgs& g, int mode, int dtype, bool wide_tri, bool coverage, const char* what) {
+void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool coverage, const char* what) {
+  const int mode = kind.mode;
   const bool tri = mode_is_tri(mode);
-  const TileCfg t = tile_cfg(dtype, tri, wide_tri);
+  const TileCfg t = tile_cfg(dtype, tri, kind.wide_tri);
   const int es = (int)elem_size(dtype);
   const int EPC = 16 / es, BK = t.cpr * EPC;
   const int NT = t.wm * t.wn * 64, WTM = t.bm / t.wm, WTN = t.bn / t.wn;
@@ -122,13 +159,11 @@ void replay_gemm(const GemmArgs& g, int mode, int dtype, bool wide_tri, bool cov
     if (g.d_out) dcover.assign((size_t)g.d_bs * g.batch, 0);
   }
   // fragment reads stay inside each operand region of a slot
-  for (int wave = 0; wave < t.wm * t.wn; ++wave)
-    for (int lane = 0; lane < 64; ++lane)
-      for (int s = 0; s < t.cpr / 2; ++s) {
-        const int ch = 2 * s + (lane >> 5), wm = wave / t.wn, wn = wave % t.wn;
-        for (int a = 0; a < SM; ++a) lds_index(lds_swz(wm * WTM + a * 32 + (lane & 31), ch, t.cpr), LP, what);
-        for (int b = 0; b < SN; ++b) lds_index(lds_swz(wn * WTN + b * 32 + (lane & 31), ch, t.cpr), LQ, what);
-      }
+  for (int wave = 0; wave < t.wm * t.wn; ++wave) {
+    const int wm = wave / t.wn, wn = wave % t.wn;
+    replay_frag_reads(t, es, kind.p_nat, t.bm, WTM, SM, wm * WTM, what);
+    replay_frag_reads(t, es, kind.q_nat, t.bn, WTN, SN, wn * WTN, what);
+  }
 
   for (int w = 0; w < G; ++w) {
     const int lin = xcd_remap(w, G);
@@ -150,7 +185,7 @@ void replay_gemm(const GemmArgs& g, int mode, int dtype, bool wide_tri, bool cov
     for (int si = 0; si < (nk > 1 ? 2 : 1); ++si) {
       const int kt = kstages[si];
       for (int wave = 0; wave < NW; ++wave)
-        replay_dma(wave, NIW, t.bm, t.cpr, es, kt * BK, g.K, g, slice, i0, j0, STAGE, kt % t.st, LDS, what);
+        replay_dma(wave, NIW, t, es, kind.p_nat, kind.q_nat, kt * BK, g, slice, i0, j0, STAGE, kt % t.st, LDS, what);
     }
     // epilogue step 1 (mirrors gemm_kernel): registers -> staged tile
     const bool diag_tile = tri && ti == tj;
@@ -234,56 +269,28 @@ void replay_gemm(const GemmArgs& g, int mode, int dtype, bool wide_tri, bool cov
   }
 }
 
-void replay_norm(const NormArgs& g, int batch, bool scale, int es, const char* what) {
+void replay_norm(const NormArgs& g, int batch, bool scale, const char* what) {
   const int NT = 256;
-  if (!scale) {
-    for (int slice = 0; slice < batch; ++slice)
-      for (int chunk = 0; chunk < g.chunks; ++chunk) {
-        const long long v0 = (long long)chunk * g.chunk_vecs;
-        const long long v1 = (v0 + g.chunk_vecs < g.slice_vecs) ? v0 + g.chunk_vecs : g.slice_vecs;
-        if (v0 >= g.slice_vecs) fail(std::string(what) + ": empty norm block");
-        for (int tid = 0; tid < NT; ++tid) {
-          const long long first = v0 + tid;
-          if (first >= v1) continue;
-          const long long last = first + ((v1 - 1 - first) / NT) * NT;
-          for (long long v : {first, last}) access(g.x, ((long long)slice * g.slice_vecs + v) * 16, 16, what);
+  for (int slice = 0; slice < batch; ++slice)
+    for (int chunk = 0; chunk < g.chunks; ++chunk) {
+      const long long v0 = (long long)chunk * g.chunk_vecs;
+      const long long v1 = (v0 + g.chunk_vecs < g.slice_vecs) ? v0 + g.chunk_vecs : g.slice_vecs;
+      if (v0 >= g.slice_vecs) fail(std::string(what) + ": empty norm block");
+      for (int tid = 0; tid < NT; ++tid) {
+        const long long first = v0 + tid;
+        if (first >= v1) continue;
+        const long long last = first + ((v1 - 1 - first) / NT) * NT;
+        for (long long v : {first, last}) {
+          access(g.x, ((long long)slice * g.slice_vecs + v) * 16, 16, what);
+          if (scale) access(g.y, ((long long)slice * g.slice_vecs + v) * 16, 16, what);
         }
+      }
+      if (scale) {
+        for (int i = 0; i < g.chunks; ++i) access(g.partials, ((long long)slice * g.chunks + i) * 4, 4, what);
+        if (g.norms) access(g.norms, (long long)slice * 4, 4, what);
+      } else {
         access(g.partials, ((long long)slice * g.chunks + chunk) * 4, 4, what);
       }
-    return;
-  }
-  const int EPC = 16 / es, TS = kScaleTile, CPT = TS / EPC, SROW = TS + EPC;
-  const long long lds_bytes = (long long)TS * SROW * es;
-  std::vector<uint8_t> cov((size_t)g.rows * g.cols, 0), tcov(g.yt ? (size_t)g.rows * g.cols : 0, 0);
-  for (int slice = 0; slice < batch; ++slice)
-    for (int blk = 0; blk < g.tiles_r * g.tiles_c; ++blk) {
-      const int tr = blk / g.tiles_c, tc = blk % g.tiles_c;
-      for (int i = 0; i < g.chunks; ++i) access(g.partials, ((long long)slice * g.chunks + i) * 4, 4, what);
-      if (g.norms) access(g.norms, (long long)slice * 4, 4, what);
-      const long long base = (long long)slice * g.rows * g.cols;
-      for (int qd = 0; qd < TS * CPT; ++qd) {
-        const int r = qd / CPT, c = qd % CPT, gr = tr * TS + r, gc = tc * TS + c * EPC;
-        if (gr >= g.rows || gc >= g.cols) continue;
-        access(g.x, (base + (long long)gr * g.cols + gc) * es, 16, what);
-        access(g.y, (base + (long long)gr * g.cols + gc) * es, 16, what);
-        if (((long long)r * SROW + c * EPC) * es + 16 > lds_bytes) fail(std::string(what) + ": scale tile LDS");
-        if (slice == 0)
-          for (int e = 0; e < EPC; ++e) cov[(size_t)gr * g.cols + gc + e]++;
-      }
-      if (!g.yt) continue;
-      for (int qd = 0; qd < TS * CPT; ++qd) {
-        const int cl = qd % TS, rc = qd / TS, gc = tc * TS + cl, gr = tr * TS + rc * EPC;
-        if (gc >= g.cols || gr >= g.rows) continue;
-        if (((long long)(rc * EPC + EPC - 1) * SROW + cl) * es + es > lds_bytes) fail(std::string(what) + ": scale LDS");
-        access(g.yt, (base + (long long)gc * g.rows + gr) * es, 16, what);
-        if (slice == 0)
-          for (int e = 0; e < EPC; ++e) tcov[(size_t)gc * g.rows + gr + e]++;
-      }
-    }
-  for (size_t i = 0; i < cov.size(); ++i)
-    if (cov[i] != 1 || (!tcov.empty() && tcov[i] != 1)) {
-      fail(std::string(what) + ": scale output not covered exactly once");
-      break;
     }
 }
 
@@ -297,32 +304,29 @@ void replay_call(int dtype, long long batch, long long rows, long long cols, int
   void* in = reg(uintptr_t(1) << 44, "in", xbytes);
   void* out = alias ? in : reg(uintptr_t(2) << 44, "out", xbytes);
   void* xtmp = reg(uintptr_t(3) << 44, "xtmp", xbytes);
-  void* xt[2] = {reg(uintptr_t(9) << 44, "xt0", xbytes), reg(uintptr_t(10) << 44, "xt1", xbytes)};
   void* oa = reg(uintptr_t(4) << 44, "oa", mm);
   void* oc = reg(uintptr_t(5) << 44, "oc", mm);
   float* da = (float*)reg(uintptr_t(6) << 44, "da", (size_t)batch * p.m * 4);
   float* dc = (float*)reg(uintptr_t(7) << 44, "dc", (size_t)batch * p.m * 4);
   float* part = (float*)reg(uintptr_t(8) << 44, "partials", (size_t)batch * p.norm_chunks * 4);
   if (p.off_part + (size_t)batch * p.norm_chunks * 4 > p.total) fail("workspace plan too small");
-  if (p.off_xt1 - p.off_xt0 < xbytes || p.off_oa - p.off_xt1 < xbytes || p.off_xt0 - p.off_xtmp < xbytes)
-    fail("workspace plan overlaps the iterate buffers");
+  if (p.off_oa - p.off_xtmp < xbytes) fail("workspace plan overlaps the iterate buffer");
 
   auto buf = [&](int s) -> void* { return iterate_in_out(steps, s) ? out : xtmp; };
-  const NormArgs ng = norm_args(p, in, buf(0), steps > 0 ? xt[0] : nullptr, nullptr, part);
-  replay_norm(ng, (int)batch, false, es, "sumsq");
-  replay_norm(ng, (int)batch, true, es, "scale");
+  const NormArgs ng = norm_args(p, in, buf(0), nullptr, part);
+  replay_norm(ng, (int)batch, false, "sumsq");
+  replay_norm(ng, (int)batch, true, "scale");
   const bool cov = (long long)batch * std::max<long long>(p.m * p.m, rows * cols) <= 80LL * 1000 * 1000;
   for (int s = 1; s <= steps; ++s) {
     if (s != 1 && s != steps) continue;  // middle steps differ only in which buffer is which
-    int mode;
-    GemmArgs g = gram_args(p, buf(s - 1), xt[(s - 1) & 1], oa, da, &mode);
-    replay_gemm(g, mode, dtype, plan_wide_tri(p), cov, "gram");
-    g = poly_args(p, oa, da, oc, dc, 3.4445f, -4.775f, 2.0315f, &mode);
-    replay_gemm(g, mode, dtype, plan_wide_tri(p), cov, "poly");
+    StageKind kind;
+    GemmArgs g = gram_args(p, buf(s - 1), oa, da, &kind);
+    replay_gemm(g, kind, dtype, cov, "gram");
+    g = poly_args(p, oa, da, oc, dc, 3.4445f, -4.775f, 2.0315f, &kind);
+    replay_gemm(g, kind, dtype, cov, "poly");
     if (buf(s - 1) == buf(s)) fail("update reads the buffer it writes");
-    void* xto = (s < steps) ? xt[s & 1] : nullptr;
-    g = update_args(p, buf(s - 1), xt[(s - 1) & 1], oc, dc, buf(s), xto, &mode);
-    replay_gemm(g, mode, dtype, false, cov, "update");
+    g = update_args(p, buf(s - 1), oc, dc, buf(s), &kind);
+    replay_gemm(g, kind, dtype, cov, "update");
   }
 }
 

@@ -5,10 +5,11 @@
 #include <stdint.h>
 
 #include "ns_layout.h"
+#include "ns_plan.h"
 
 namespace ns {
 
-hipError_t launch_gemm(int dtype, int mode, bool wide_tri, const GemmArgs& g, hipStream_t st);
+hipError_t launch_gemm(int dtype, const StageKind& k, const GemmArgs& g, hipStream_t st);
 hipError_t launch_sumsq(int dtype, const NormArgs& g, int batch, hipStream_t st);
 hipError_t launch_scale(int dtype, const NormArgs& g, int batch, hipStream_t st);
 

@@ -11,13 +11,14 @@
 // never pass through bf16 (the page credits fp32 epilogue arithmetic for the
 // symmetric path's accuracy; this placement extends that to the diagonals).
 //
-// The iterate is kept in HBM in both orientations, X and Xᵀ (the update
-// writes both from its staged output tile), so that every operand of every
-// product is read as K-contiguous rows:
-//   Gram, rows <= cols: P = Q = rows of X
-//   Gram, rows >  cols: P = Q = rows of Xᵀ
-//   poly:               P = Q = rows of O_A      (A symmetric: A A = A Aᵀ)
-//   update, wide:       P = rows of O_C, Q = rows of Xᵀ   (X' = C X)
+// The iterate is kept in HBM only in the input's orientation.  An operand is
+// read either as K-contiguous rows (staged as chunks along k) or, where the
+// reduction runs down the columns of the stored matrix, in its natural layout
+// (staged as k rows and read back transposed with ds_read_b64_tr_b16):
+//   Gram, rows <= cols: P = Q = rows of X                 (K-contiguous)
+//   Gram, rows >  cols: P = Q = columns of X              (natural layout)
+//   poly:               P = Q = rows of O_A  (A symmetric: A A = A Aᵀ)
+//   update, wide:       P = rows of O_C, Q = columns of X (X' = C X)
 //   update, tall:       P = rows of X,   Q = rows of O_C  (X' = X C)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -26,6 +27,7 @@
 
 #include "ns_kernels.h"
 #include "ns_layout.h"
+#include "ns_plan.h"
 
 namespace ns {
 
@@ -131,8 +133,38 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int CPR, int ST, int MODE>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// One MFMA operand fragment (8 bf16 or 4 fp32 k values of one tile row, the
+// same k assignment as a K-contiguous chunk) from a NAT tile in LDS.
+__device__ __forceinline__ uint4 nat_frag(const uint4* tile, int rc, int s, int rb, int lane, bf16) {
+  uint32_t w[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int kr = nat_tr_kr(s, h, lane), col = nat_tr_col(rb, lane);
+    const int pos = kr * rc + ((col >> 3) ^ nat_swz(kr, rc, 2));
+    const short* src = reinterpret_cast<const short*>(tile + pos) + (col & 7);
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)src);
+    w[2 * h] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+    w[2 * h + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ uint4 nat_frag(const uint4* tile, int rc, int s, int rb, int lane, float) {
+  // k = 8 s + 4 (lane / 32) + e, column rb + lane % 32
+  const int col = rb + (lane & 31);
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int kr = 8 * s + 4 * (lane >> 5) + e;
+    const int pos = kr * rc + ((col >> 2) ^ nat_swz(kr, rc, 4));
+    w[e] = reinterpret_cast<const uint32_t*>(tile + pos)[col & 3];
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int CPR, int ST, int OCC, int MODE, bool PNAT, bool QNAT>
+__global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g) {
   constexpr int NT = WM * WN * 64, NW = WM * WN;
   constexpr int EPC = Elem<T>::kChunk;
   constexpr int ES = (int)sizeof(T);
@@ -143,6 +175,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   constexpr int STAGE = LP + LQ;
   constexpr int NIW = STAGE / 64 / NW;         // load instructions per wave per stage
   constexpr int ERC = epi_row_chunks(BN, ES);  // staged output row, in chunks
+  constexpr int RCP = BM / EPC, RCQ = BN / EPC;  // chunks per k row of a NAT tile
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(!mode_is_tri(MODE) || BM == BN, "triangle modes need square tiles");
   static_assert(CPR == 4 || CPR == 8 || CPR == 16, "4, 8 or 16 chunks per LDS row");
@@ -171,24 +204,29 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
   const i32x4 rQ = make_rsrc(Qbase, (unsigned)(g.q_bs * ES));
   constexpr unsigned kOutOfRange = 0x80000000u;
 
-  // per-lane source of each of this wave's load instructions (same every stage)
-  unsigned src_off[NIW];
+  // per-lane source of each of this wave's load instructions: byte offset at
+  // k0 = 0, k position within the stage (>= K means zero fill), and the
+  // byte step from one stage to the next
+  unsigned src_off[NIW], src_step[NIW];
   int src_k[NIW];
 #pragma unroll
   for (int t = 0; t < NIW; ++t) {
-    const DmaSrc d = dma_src(wave * NIW + t, lane, BM, CPR);
-    const int grow = (d.is_p ? i0 : j0) + d.row;
-    const bool rowok = grow < (d.is_p ? g.M : g.N);
+    const DmaSrc d = dma_src(wave * NIW + t, lane, BM, BN, CPR, EPC, PNAT, QNAT, ES);
+    const bool nat = d.is_p ? PNAT : QNAT;
     const int ld = d.is_p ? g.ldp : g.ldq;
-    src_off[t] = rowok ? (unsigned)(((size_t)grow * ld + d.ch * EPC) * ES) : kOutOfRange;
-    src_k[t] = rowok ? d.ch * EPC : g.K;  // k offset of the chunk; >= K means zero
+    const int g_row = (d.is_p ? i0 : j0) + d.row;  // tile row (KCONT) or column (NAT)
+    const bool ok = g_row < (d.is_p ? g.M : g.N);
+    const size_t off = nat ? ((size_t)d.kpos * ld + g_row) * ES : ((size_t)g_row * ld + d.kpos) * ES;
+    src_off[t] = ok ? (unsigned)off : kOutOfRange;
+    src_k[t] = ok ? d.kpos : g.K;
+    src_step[t] = nat ? (unsigned)(BK * ld * ES) : (unsigned)(BK * ES);
   }
   auto issue = [&](int kt, int slot) {
     const int k0 = kt * BK;
 #pragma unroll
     for (int t = 0; t < NIW; ++t) {
       const int idx = wave * NIW + t;  // wave-uniform
-      const unsigned off = (k0 + src_k[t] < g.K) ? src_off[t] + (unsigned)(k0 * ES) : kOutOfRange;
+      const unsigned off = (k0 + src_k[t] < g.K) ? src_off[t] + (unsigned)kt * src_step[t] : kOutOfRange;
       const unsigned dst = lds_addr(lds + slot * STAGE + idx * 64);
       dma16(dst, off, idx * 64 < LP ? rP : rQ);
     }
@@ -211,9 +249,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(const GemmArgs g) {
       const int ch = 2 * s + half;
       uint4 pf[SM], qf[SN];
 #pragma unroll
-      for (int a = 0; a < SM; ++a) pf[a] = Ps[lds_swz(wm * WTM + a * 32 + l32, ch, CPR)];
+      for (int a = 0; a < SM; ++a)
+        pf[a] = PNAT ? nat_frag(Ps, RCP, s, wm * WTM + a * 32, lane, T())
+                     : Ps[lds_swz(wm * WTM + a * 32 + l32, ch, CPR)];
 #pragma unroll
-      for (int b = 0; b < SN; ++b) qf[b] = Qs[lds_swz(wn * WTN + b * 32 + l32, ch, CPR)];
+      for (int b = 0; b < SN; ++b)
+        qf[b] = QNAT ? nat_frag(Qs, RCQ, s, wn * WTN + b * 32, lane, T())
+                     : Qs[lds_swz(wn * WTN + b * 32 + l32, ch, CPR)];
 #pragma unroll
       for (int a = 0; a < SM; ++a)
 #pragma unroll
@@ -416,19 +458,12 @@ __global__ __launch_bounds__(kNormThreads) void sumsq_kernel(const NormArgs g) {
 }
 
 // Pass 2: every block sums its slice's partials (same order in every block),
-// then scales one 64 x 64 tile: X0 = x / (sqrt(sum) + eps) written row-wise,
-// and (if yt is set) X0ᵀ written through an LDS transpose.
+// then writes x / (sqrt(sum) + eps) for the same 32 KiB block, in place if
+// y == x (each element is read and written by the same thread).
 template <typename T>
 __global__ __launch_bounds__(kNormThreads) void scale_kernel(const NormArgs g) {
-  constexpr int EPC = Elem<T>::kChunk;
-  constexpr int TS = kScaleTile;
-  constexpr int CPT = TS / EPC;           // chunks per tile row
-  constexpr int SROW = TS + EPC;          // padded LDS row, elements
   __shared__ float s_inv;
-  __shared__ uint4 tile_raw[TS * SROW / EPC];
-  T* tile = reinterpret_cast<T*>(tile_raw);
-  const int slice = blockIdx.y;
-  const int tr = blockIdx.x / g.tiles_c, tc = blockIdx.x % g.tiles_c;
+  const int slice = blockIdx.y, chunk = blockIdx.x;
   if (threadIdx.x < 64) {
     float s = 0.0f;
     for (int i = threadIdx.x; i < g.chunks; i += 64) s += g.partials[(size_t)slice * g.chunks + i];
@@ -436,62 +471,50 @@ __global__ __launch_bounds__(kNormThreads) void scale_kernel(const NormArgs g) {
     if (threadIdx.x == 0) {
       const float nrm = sqrtf(s);
       s_inv = 1.0f / (nrm + g.eps);
-      if (g.norms != nullptr && blockIdx.x == 0) g.norms[slice] = nrm;
+      if (g.norms != nullptr && chunk == 0) g.norms[slice] = nrm;
     }
   }
   __syncthreads();
   const float inv = s_inv;
-  const size_t base = (size_t)slice * g.rows * g.cols;
-  const T* x = reinterpret_cast<const T*>(g.x) + base;
-  T* y = reinterpret_cast<T*>(g.y) + base;
-  for (int qd = threadIdx.x; qd < TS * CPT; qd += kNormThreads) {
-    const int r = qd / CPT, c = qd % CPT;
-    const int gr = tr * TS + r, gc = tc * TS + c * EPC;
-    if (gr >= g.rows || gc >= g.cols) continue;
-    const uint4 v = scale16(ldg16(x + (size_t)gr * g.cols + gc), inv, T());
-    *reinterpret_cast<uint4*>(y + (size_t)gr * g.cols + gc) = v;
-    *reinterpret_cast<uint4*>(tile + r * SROW + c * EPC) = v;
-  }
-  if (g.yt == nullptr) return;  // uniform across the block
-  __syncthreads();
-  T* yt = reinterpret_cast<T*>(g.yt) + base;
-  for (int qd = threadIdx.x; qd < TS * CPT; qd += kNormThreads) {
-    const int cl = qd % TS, rc = qd / TS;  // tile column cl, rows [EPC rc, +EPC)
-    const int gc = tc * TS + cl, gr = tr * TS + rc * EPC;
-    if (gc >= g.cols || gr >= g.rows) continue;
-    T tmp[EPC];
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) tmp[e] = tile[(rc * EPC + e) * SROW + cl];
-    *reinterpret_cast<uint4*>(yt + (size_t)gc * g.rows + gr) = *reinterpret_cast<const uint4*>(tmp);
-  }
+  const uint4* xv = reinterpret_cast<const uint4*>(g.x) + (size_t)slice * g.slice_vecs;
+  uint4* yv = reinterpret_cast<uint4*>(g.y) + (size_t)slice * g.slice_vecs;
+  const long long v0 = (long long)chunk * g.chunk_vecs;
+  const long long v1 = (v0 + g.chunk_vecs < g.slice_vecs) ? v0 + g.chunk_vecs : g.slice_vecs;
+  for (long long v = v0 + threadIdx.x; v < v1; v += kNormThreads) yv[v] = scale16(xv[v], inv, T());
 }
 
 // ------------------------------------------------------------- launchers
 
-template <typename T, int MODE, bool WIDE>
+template <typename T, int MODE, bool WIDE, bool PNAT, bool QNAT>
 static hipError_t launch_mode(const GemmArgs& g, hipStream_t st) {
   constexpr TileCfg t = tile_cfg(std::is_same<T, bf16>::value ? 1 : 0, mode_is_tri(MODE), WIDE);
   const int total = g.tiles_per_slice * g.batch;
-  hipLaunchKernelGGL((gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.cpr, t.st, MODE>), dim3(total),
-                     dim3(t.wm * t.wn * 64), 0, st, g);
+  hipLaunchKernelGGL((gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.cpr, t.st, t.occ, MODE, PNAT, QNAT>),
+                     dim3(total), dim3(t.wm * t.wn * 64), 0, st, g);
   return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t dispatch_mode(int mode, bool wide_tri, const GemmArgs& g, hipStream_t st) {
-  const bool wide = wide_tri && std::is_same<T, bf16>::value;
-  switch (mode) {
-    case MODE_GRAM: return wide ? launch_mode<T, MODE_GRAM, true>(g, st) : launch_mode<T, MODE_GRAM, false>(g, st);
-    case MODE_POLY: return wide ? launch_mode<T, MODE_POLY, true>(g, st) : launch_mode<T, MODE_POLY, false>(g, st);
-    case MODE_UPD_ROW: return launch_mode<T, MODE_UPD_ROW, false>(g, st);
-    case MODE_UPD_COL: return launch_mode<T, MODE_UPD_COL, false>(g, st);
+static hipError_t dispatch_mode(const StageKind& k, const GemmArgs& g, hipStream_t st) {
+  const bool wide = k.wide_tri && std::is_same<T, bf16>::value;
+  switch (k.mode) {
+    case MODE_GRAM:
+      if (k.p_nat) return wide ? launch_mode<T, MODE_GRAM, true, true, true>(g, st)
+                               : launch_mode<T, MODE_GRAM, false, true, true>(g, st);
+      return wide ? launch_mode<T, MODE_GRAM, true, false, false>(g, st)
+                  : launch_mode<T, MODE_GRAM, false, false, false>(g, st);
+    case MODE_POLY:
+      return wide ? launch_mode<T, MODE_POLY, true, false, false>(g, st)
+                  : launch_mode<T, MODE_POLY, false, false, false>(g, st);
+    case MODE_UPD_ROW: return launch_mode<T, MODE_UPD_ROW, false, false, true>(g, st);
+    case MODE_UPD_COL: return launch_mode<T, MODE_UPD_COL, false, false, false>(g, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_gemm(int dtype, int mode, bool wide_tri, const GemmArgs& g, hipStream_t st) {
-  if (dtype == 1) return dispatch_mode<bf16>(mode, wide_tri, g, st);
-  return dispatch_mode<float>(mode, wide_tri, g, st);
+hipError_t launch_gemm(int dtype, const StageKind& k, const GemmArgs& g, hipStream_t st) {
+  if (dtype == 1) return dispatch_mode<bf16>(k, g, st);
+  return dispatch_mode<float>(k, g, st);
 }
 
 hipError_t launch_sumsq(int dtype, const NormArgs& g, int batch, hipStream_t st) {
@@ -502,7 +525,7 @@ hipError_t launch_sumsq(int dtype, const NormArgs& g, int batch, hipStream_t st)
 }
 
 hipError_t launch_scale(int dtype, const NormArgs& g, int batch, hipStream_t st) {
-  dim3 grid(g.tiles_r * g.tiles_c, batch);
+  dim3 grid(g.chunks, batch);
   if (dtype == 1) hipLaunchKernelGGL(scale_kernel<bf16>, grid, dim3(kNormThreads), 0, st, g);
   else hipLaunchKernelGGL(scale_kernel<float>, grid, dim3(kNormThreads), 0, st, g);
   return hipGetLastError();

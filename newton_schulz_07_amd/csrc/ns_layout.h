@@ -29,25 +29,26 @@ NS_HD constexpr bool mode_is_tri(int mode) { return mode == MODE_GRAM || mode ==
 // Tile shape of one kernel instance: BM x BN output tile, WM x WN waves of
 // 64 lanes, CPR 16-byte chunks per LDS row (K stage = CPR * 16 bytes of each
 // operand row), ST = K stages held in the LDS ring (loads run ST-1 stages
-// ahead of the MFMAs).
+// ahead of the MFMAs), OCC = workgroups per CU the register budget is sized
+// for.
 struct TileCfg {
-  int bm, bn, wm, wn, cpr, st;
+  int bm, bn, wm, wn, cpr, st, occ;
 };
 
 #ifndef NS_TILE_BF16_TRI
-#define NS_TILE_BF16_TRI {128, 128, 2, 4, 8, 2}
+#define NS_TILE_BF16_TRI {128, 128, 2, 4, 8, 2, 2}
 #endif
 #ifndef NS_TILE_BF16_TRI_WIDE
-#define NS_TILE_BF16_TRI_WIDE {192, 192, 2, 2, 8, 2}
+#define NS_TILE_BF16_TRI_WIDE {192, 192, 2, 2, 8, 2, 1}
 #endif
 #ifndef NS_TILE_BF16_RECT
-#define NS_TILE_BF16_RECT {256, 256, 2, 4, 8, 2}
+#define NS_TILE_BF16_RECT {256, 256, 2, 4, 8, 2, 1}
 #endif
 #ifndef NS_TILE_F32_TRI
-#define NS_TILE_F32_TRI {128, 128, 2, 2, 8, 3}
+#define NS_TILE_F32_TRI {128, 128, 2, 2, 8, 3, 1}
 #endif
 #ifndef NS_TILE_F32_RECT
-#define NS_TILE_F32_RECT {128, 128, 2, 2, 8, 3}
+#define NS_TILE_F32_RECT {128, 128, 2, 2, 8, 3, 1}
 #endif
 constexpr TileCfg kTileBf16Tri = NS_TILE_BF16_TRI;
 constexpr TileCfg kTileBf16TriWide = NS_TILE_BF16_TRI_WIDE;
@@ -122,22 +123,53 @@ NS_HD int swz_f(int row, int cpr) {
 }
 NS_HD int lds_swz(int row, int ch, int cpr) { return row * cpr + (ch ^ swz_f(row, cpr)); }
 
+// An operand is read either as K-contiguous rows (KCONT: element (i, k) at
+// base + i ld + k) or in its natural layout (NAT: element (i, k) at
+// base + k ld + i, i.e. rows of the stored matrix are the k index).  A NAT
+// stage sits in LDS as BK rows (k) of R / EPC chunks (i); chunk c of k-row kr
+// is stored at position c ^ nat_swz(kr), which keeps the transposed fragment
+// reads below free of bank conflicts (checked for R = 128, 192, 256 bf16 and
+// R = 128 fp32).
+NS_HD int nat_swz(int kr, int row_chunks, int esize) {
+  if (esize == 4) return (kr & 7) << 1;
+  return row_chunks % 16 == 0 ? (kr & 3) << 2 : (kr >> 1) & 7;
+}
+
 // Loader: each wave instruction fills 64 consecutive chunks of a stage (one
 // 16-byte chunk per lane).  Instruction idx of a stage covers chunk positions
-// [64 idx, 64 idx + 64): the P rows first, then the Q rows.
+// [64 idx, 64 idx + 64): the P tile first, then the Q tile.  For a KCONT tile
+// `row` is the tile row and `kpos` the k offset (in elements) of the lane's
+// chunk; for a NAT tile `row` is the tile column (first of EPC) and `kpos`
+// the k row.
 struct DmaSrc {
   bool is_p;     // operand P (else Q)
-  int row;       // row of the operand tile
-  int ch;        // logical chunk (k offset ch * 16 bytes) loaded by this lane
+  int row;       // tile row (KCONT) or first tile column of the chunk (NAT)
+  int kpos;      // k offset within the stage
   int lds_pos;   // chunk position in the stage slot written by this lane
 };
-NS_HD DmaSrc dma_src(int idx, int lane, int bm, int cpr) {
+NS_HD DmaSrc dma_src(int idx, int lane, int bm, int bn, int cpr, int epc, bool p_nat, bool q_nat, int esize) {
   const int p = idx * 64 + lane;
   const bool is_p = p < bm * cpr;
   const int pp = is_p ? p : p - bm * cpr;
-  const int row = pp / cpr, phys = pp % cpr;
-  return DmaSrc{is_p, row, phys ^ swz_f(row, cpr), p};
+  const bool nat = is_p ? p_nat : q_nat;
+  if (!nat) {
+    const int row = pp / cpr, phys = pp % cpr;
+    return DmaSrc{is_p, row, (phys ^ swz_f(row, cpr)) * epc, p};
+  }
+  const int rc = (is_p ? bm : bn) / epc;  // chunks per k row
+  const int kr = pp / rc, phys = pp % rc;
+  return DmaSrc{is_p, (phys ^ nat_swz(kr, rc, esize)) * epc, kr, p};
 }
+
+// Transposed fragment read of a NAT bf16 tile with ds_read_b64_tr_b16.  In a
+// group of 16 lanes, lane t receives element t % 4 of the 4-element vectors
+// addressed by lanes 4e + t / 4 (e = 0..3).  With lane l addressing k row
+// 16 s + 8 (l / 32) + 4 h + (l % 16) / 4 and columns rb + 16 ((l / 16) % 2) +
+// 4 (l % 4) .. +3, lane l receives column rb + l % 32 at k rows
+// 16 s + 8 (l / 32) + 4 h + 0..3: two reads (h = 0, 1) give the same 8 k
+// values per lane as a K-contiguous chunk read.
+NS_HD int nat_tr_kr(int s, int h, int lane) { return 16 * s + 8 * (lane >> 5) + 4 * h + ((lane & 15) >> 2); }
+NS_HD int nat_tr_col(int rb, int lane) { return rb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3); }
 
 // MFMA operand roles: the A operand is the Q tile (output column j), the B
 // operand the P tile (output row i).  Register r of lane l of a 32x32 block
@@ -148,8 +180,9 @@ NS_HD int acc_j(int rgroup, int lane) { return 8 * rgroup + 4 * (lane >> 5); }
 
 // Arguments of one tiled MFMA launch over `batch` slices.  The kernel forms
 // acc(i, j) = sum_k P(i, k) Q(j, k) over an M x N output with reduction
-// length K (both operands K-contiguous), applies the mode's epilogue, stores
-// the tile to `out` and, if out_t is set, its transpose to out_t.
+// length K (each operand KCONT or NAT, a template choice), applies the mode's
+// epilogue, stores the tile to `out` and, if out_t is set, its transpose to
+// out_t.
 struct GemmArgs {
   const void* P;      // operand P rows, slice 0
   const void* Q;      // operand Q rows, slice 0
@@ -173,21 +206,16 @@ struct GemmArgs {
   float ca, cb, cc;   // quintic coefficients (poly only)
 };
 
-// Normalisation: per-slice sum of squares over 32 KiB blocks, then a 2-D
-// tiled scale pass that writes X0 and X0ᵀ.
-constexpr int kScaleTile = 64;   // scale pass: 64 x 64 element tiles
-
+// Normalisation: per-slice sum of squares over 32 KiB blocks, then a scale
+// pass over the same blocks.
 struct NormArgs {
   const void* x;         // input  [batch, rows, cols]
   void* y;               // X0 [batch, rows, cols] (scale pass), may equal x
-  void* yt;              // X0ᵀ [batch, cols, rows] (scale pass), or null
   float* partials;       // [batch, chunks] sums of squares
   float* norms;          // optional [batch] Frobenius norms (scale pass)
   long long slice_vecs;  // 16-byte vectors per slice
-  long long chunk_vecs;  // 16-byte vectors per sum-of-squares block
-  int chunks;            // sum-of-squares blocks per slice
-  int rows, cols;
-  int tiles_r, tiles_c;  // scale-pass tiles per slice
+  long long chunk_vecs;  // 16-byte vectors per block
+  int chunks;            // blocks per slice
   float eps;
 };
 

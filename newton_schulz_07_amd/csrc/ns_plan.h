@@ -25,7 +25,7 @@ struct Plan {
   int dtype;
   int norm_chunks;
   // workspace offsets (bytes)
-  size_t off_xtmp, off_xt0, off_xt1, off_oa, off_oc, off_da, off_dc, off_part, total;
+  size_t off_xtmp, off_oa, off_oc, off_da, off_dc, off_part, total;
 };
 
 inline Plan make_plan(int64_t batch, int64_t rows, int64_t cols, int dtype) {
@@ -40,14 +40,9 @@ inline Plan make_plan(int64_t batch, int64_t rows, int64_t cols, int dtype) {
   const size_t es = elem_size(dtype);
   const long long vecs = rows * cols * (long long)es / 16;
   p.norm_chunks = (int)((vecs + kNormChunkVecs - 1) / kNormChunkVecs);
-  const size_t xbytes = ws_align((size_t)batch * rows * cols * es);
   size_t off = 0;
   p.off_xtmp = off;
-  off += xbytes;
-  p.off_xt0 = off;
-  off += xbytes;
-  p.off_xt1 = off;
-  off += xbytes;
+  off += ws_align((size_t)batch * rows * cols * es);
   p.off_oa = off;
   off += ws_align((size_t)batch * p.m * p.m * es);
   p.off_oc = off;
@@ -64,38 +59,39 @@ inline Plan make_plan(int64_t batch, int64_t rows, int64_t cols, int dtype) {
 
 // The iterate X_s (s = 0 after normalisation) is held in `out` when
 // (steps - s) is even and in the workspace temporary otherwise, so the last
-// step writes `out` and no update reads the buffer it writes.  Its transpose
-// X_sᵀ alternates between two workspace buffers (xt0 for even s).
+// step writes `out` and no update reads the buffer it writes.
 inline bool iterate_in_out(int steps, int s) { return ((steps - s) % 2) == 0; }
 
-inline NormArgs norm_args(const Plan& p, const void* x, void* y, void* yt, float* norms, float* partials) {
+inline NormArgs norm_args(const Plan& p, const void* x, void* y, float* norms, float* partials) {
   NormArgs g{};
   g.x = x;
   g.y = y;
-  g.yt = yt;
   g.partials = partials;
   g.norms = norms;
   g.slice_vecs = p.rows * p.cols * (long long)elem_size(p.dtype) / 16;
   g.chunk_vecs = kNormChunkVecs;
   g.chunks = p.norm_chunks;
-  g.rows = (int)p.rows;
-  g.cols = (int)p.cols;
-  g.tiles_r = tiles_of(p.rows, kScaleTile);
-  g.tiles_c = tiles_of(p.cols, kScaleTile);
   g.eps = kNormEps;
   return g;
 }
 
-// A = X Xᵀ (rows <= cols: rows of X) or Xᵀ X (rows > cols: rows of Xᵀ),
-// mirrored into the same m x m matrix.
+// Which kernel instance a stage launches.
+struct StageKind {
+  int mode;
+  bool p_nat, q_nat;  // operand read in its natural layout (see ns_layout.h)
+  bool wide_tri;      // 192 x 192 triangle tile
+};
+
 inline bool plan_wide_tri(const Plan& p) { return use_wide_tri(p.dtype, p.batch, p.m); }
 
-inline GemmArgs gram_args(const Plan& p, const void* x, const void* xt, void* oa, float* da, int* mode) {
+// A = X Xᵀ (rows <= cols: rows of X are K-contiguous) or Xᵀ X (rows > cols:
+// columns of X, read in X's natural layout), mirrored into one m x m matrix.
+inline GemmArgs gram_args(const Plan& p, const void* x, void* oa, float* da, StageKind* kind) {
   const TileCfg t = tile_cfg(p.dtype, true, plan_wide_tri(p));
   GemmArgs g{};
-  g.P = g.Q = p.tall ? xt : x;
+  g.P = g.Q = x;
   g.p_bs = g.q_bs = p.rows * p.cols;
-  g.ldp = g.ldq = (int)p.n;
+  g.ldp = g.ldq = (int)p.cols;
   g.M = g.N = (int)p.m;
   g.K = (int)p.n;
   g.tiles_m = g.tiles_n = tiles_of(p.m, t.bm);
@@ -106,13 +102,13 @@ inline GemmArgs gram_args(const Plan& p, const void* x, const void* xt, void* oa
   g.ldo = g.ldt = (int)p.m;
   g.d_out = da;
   g.d_bs = p.m;
-  *mode = MODE_GRAM;
+  *kind = StageKind{MODE_GRAM, p.tall, p.tall, plan_wide_tri(p)};
   return g;
 }
 
 // C = a I + b A + c A A from the split A, written split the same way.
 inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* oc, float* dc, float a,
-                          float b, float c, int* mode) {
+                          float b, float c, StageKind* kind) {
   const TileCfg t = tile_cfg(p.dtype, true, plan_wide_tri(p));
   GemmArgs g{};
   g.P = g.Q = oa;
@@ -134,24 +130,23 @@ inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* 
   g.ca = a;
   g.cb = b;
   g.cc = c;
-  *mode = MODE_POLY;
+  *kind = StageKind{MODE_POLY, false, false, plan_wide_tri(p)};
   return g;
 }
 
-// X' = C X (rows <= cols) or X C (rows > cols), C = O_C + diag(d_C); writes
-// X' and, when xto is set, X'ᵀ.
-inline GemmArgs update_args(const Plan& p, const void* x, const void* xt, const void* oc, const float* dc,
-                            void* xo, void* xto, int* mode) {
+// X' = C X (rows <= cols) or X C (rows > cols), C = O_C + diag(d_C).
+inline GemmArgs update_args(const Plan& p, const void* x, const void* oc, const float* dc, void* xo,
+                            StageKind* kind) {
   const TileCfg t = tile_cfg(p.dtype, false);
   GemmArgs g{};
-  if (!p.tall) {  // P = rows of O_C, Q = rows of Xᵀ (columns of X)
+  if (!p.tall) {  // P = rows of O_C, Q(j, k) = X[k][j] (natural layout)
     g.P = oc;
     g.p_bs = p.m * p.m;
     g.ldp = (int)p.m;
-    g.Q = xt;
+    g.Q = x;
     g.q_bs = p.rows * p.cols;
-    g.ldq = (int)p.rows;
-    *mode = MODE_UPD_ROW;
+    g.ldq = (int)p.cols;
+    *kind = StageKind{MODE_UPD_ROW, false, true, false};
   } else {  // P = rows of X, Q = rows of O_C (C is symmetric)
     g.P = x;
     g.p_bs = p.rows * p.cols;
@@ -159,7 +154,7 @@ inline GemmArgs update_args(const Plan& p, const void* x, const void* xt, const 
     g.Q = oc;
     g.q_bs = p.m * p.m;
     g.ldq = (int)p.m;
-    *mode = MODE_UPD_COL;
+    *kind = StageKind{MODE_UPD_COL, false, false, false};
   }
   g.M = (int)p.rows;
   g.N = (int)p.cols;
@@ -171,9 +166,7 @@ inline GemmArgs update_args(const Plan& p, const void* x, const void* xt, const 
   g.out = xo;
   g.o_bs = p.rows * p.cols;
   g.ldo = (int)p.cols;
-  g.out_t = xto;
-  g.ot_bs = p.rows * p.cols;
-  g.ldt = (int)p.rows;
+  g.out_t = nullptr;
   g.E = x;
   g.e_bs = p.rows * p.cols;
   g.lde = (int)p.cols;
