@@ -187,9 +187,47 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
       for (int wave = 0; wave < NW; ++wave)
         replay_dma(wave, NIW, t, es, kind.p_nat, kind.q_nat, kt * BK, g, slice, i0, j0, STAGE, kt % t.st, LDS, what);
     }
+    // epilogue operands captured from the K stages (mirrors capture())
+    const long long db0 = (long long)slice * g.d_bs;
+    const int RCQ = t.bn / EPC;
+    for (int kt = 0; kt < nk && mode != MODE_GRAM; ++kt) {
+      const int k0 = kt * BK, slot = kt % t.st;
+      for (int tid = 0; tid < NT; ++tid) {
+        const int lane = tid & 63, wave = tid >> 6, wm = wave / t.wn, wn = wave % t.wn;
+        if (mode == MODE_UPD_ROW) {
+          for (int a = 0; a < SM; ++a) {
+            const int ib = i0 + wm * WTM + a * 32;
+            if (kt == 0 && ib + (lane & 31) < g.M) access(g.d_in, (db0 + ib + (lane & 31)) * 4, 4, what);
+            if (ib < k0 || ib >= k0 + BK) continue;
+            const int kr = ib - k0 + (lane & 31);
+            for (int b = 0; b < SN; ++b)
+              for (int rg = 0; rg < 4; ++rg) {
+                const int jl = wn * WTN + b * 32 + acc_j(rg, lane);
+                const int c = (jl / EPC) ^ nat_swz(kr, RCQ, es);
+                if (kr >= BK || c >= RCQ) fail(std::string(what) + ": capture read outside the NAT tile");
+                lds_index(slot * STAGE + LP + kr * RCQ + c, LDS, what);
+              }
+          }
+        } else {
+          for (int b = 0; b < SN; ++b) {
+            const int jb = j0 + wn * WTN + b * 32;
+            if (jb < k0 || jb >= k0 + BK) continue;
+            for (int rg = 0; rg < 4; ++rg) {
+              const int j = jb + acc_j(rg, lane), kk = j - k0;
+              if (mode == MODE_UPD_COL && j < g.N) access(g.d_in, (db0 + j) * 4, 16, what);
+              for (int a = 0; a < SM; ++a) {
+                const int il = wm * WTM + a * 32 + (lane & 31);
+                if (kk / EPC >= t.cpr) fail(std::string(what) + ": capture chunk outside the stage");
+                lds_index(slot * STAGE + lds_swz(il, kk / EPC, t.cpr), slot * STAGE + LP, what);
+              }
+            }
+          }
+        }
+      }
+    }
     // epilogue step 1 (mirrors gemm_kernel): registers -> staged tile
     const bool diag_tile = tri && ti == tj;
-    const long long ob = (long long)slice * g.o_bs, eb = (long long)slice * g.e_bs, db = (long long)slice * g.d_bs;
+    const long long ob = (long long)slice * g.o_bs, db = (long long)slice * g.d_bs;
     const int qsz = 4 * es;  // bytes of 4 consecutive elements
     for (int tid = 0; tid < NT; ++tid) {
       const int lane = tid & 63, wave = tid >> 6, wm = wave / t.wn, wn = wave % t.wn;
@@ -205,7 +243,6 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
               fail(std::string(what) + ": staged write outside LDS or misaligned");
             if (mode == MODE_GRAM || mode == MODE_POLY) {
               if (mode == MODE_POLY) {
-                access(g.E, (eb + (long long)i * g.lde + j) * es, qsz, what);
                 access(g.d_in, (db + j) * 4, 16, what);
                 access(g.d_in, (db + i) * 4, 4, what);
               }
@@ -214,9 +251,6 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
                   access(g.d_out, (db + i) * 4, 4, what);
                   if (coverage) dcover[db + i]++;
                 }
-            } else {
-              access(g.E, (eb + (long long)i * g.lde + j) * es, qsz, what);
-              access(g.d_in, (db + (mode == MODE_UPD_ROW ? i : j)) * 4, mode == MODE_UPD_ROW ? 4 : 16, what);
             }
           }
       }

@@ -263,6 +263,86 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
     }
   };
 
+  // Epilogue operands captured while they pass through LDS.  The update's
+  // diagonal term d_C ⊙ X needs X at the output position, which is the
+  // operand stage whose k range covers the tile's rows (wide: Q = columns of
+  // X, k = output row) or columns (tall: P = rows of X, k = output column):
+  // it is folded into the fp32 accumulators there.  The poly epilogue needs
+  // O_A at the output position, the P stage at k = output column: kept in
+  // registers until the epilogue.
+  typedef typename Quad<T>::Raw QRaw;
+  const float* din = g.d_in + (size_t)slice * g.d_bs;
+  float drow[SM];
+  QRaw obuf[MODE == MODE_POLY ? SM : 1][MODE == MODE_POLY ? SN : 1][4];
+  if (MODE == MODE_UPD_ROW) {
+#pragma unroll
+    for (int a = 0; a < SM; ++a) {
+      const int i = i0 + wm * WTM + a * 32 + l32;
+      drow[a] = i < g.M ? din[i] : 0.0f;
+    }
+  }
+  if (MODE == MODE_POLY) {
+#pragma unroll
+    for (int a = 0; a < SM; ++a)
+#pragma unroll
+      for (int b = 0; b < SN; ++b)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) obuf[a][b][rg] = QRaw{};
+  }
+  auto capture = [&](int slot, int kt) {
+    const int k0 = kt * BK;
+    const uint4* Ps = lds + slot * STAGE;
+    const uint4* Qs = Ps + LP;
+    if (MODE == MODE_UPD_ROW) {
+#pragma unroll
+      for (int a = 0; a < SM; ++a) {
+        const int ib = i0 + wm * WTM + a * 32;  // wave-uniform, 32-aligned
+        if (ib < k0 || ib >= k0 + BK) continue;
+        const int kr = ib - k0 + l32;
+#pragma unroll
+        for (int b = 0; b < SN; ++b)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int jl = wn * WTN + b * 32 + acc_j(rg, lane);
+            const int pos = kr * RCQ + ((jl / EPC) ^ nat_swz(kr, RCQ, ES));
+            float x[4];
+            Quad<T>::unpack(*reinterpret_cast<const QRaw*>(reinterpret_cast<const T*>(Qs + pos) + jl % EPC), x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[a][b][4 * rg + e] += drow[a] * x[e];
+          }
+      }
+    } else if (MODE == MODE_UPD_COL || MODE == MODE_POLY) {
+#pragma unroll
+      for (int b = 0; b < SN; ++b) {
+        const int jb = j0 + wn * WTN + b * 32;  // wave-uniform, 32-aligned
+        if (jb < k0 || jb >= k0 + BK) continue;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int j = jb + acc_j(rg, lane);
+          const int kk = j - k0;
+          float4 dj = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          if (MODE == MODE_UPD_COL && j < g.N) dj = *reinterpret_cast<const float4*>(din + j);
+#pragma unroll
+          for (int a = 0; a < SM; ++a) {
+            const int il = wm * WTM + a * 32 + l32;
+            const QRaw raw = *reinterpret_cast<const QRaw*>(
+                reinterpret_cast<const T*>(Ps + lds_swz(il, kk / EPC, CPR)) + kk % EPC);
+            if (MODE == MODE_POLY) {
+              obuf[a][b][rg] = raw;
+            } else {
+              float x[4];
+              Quad<T>::unpack(raw, x);
+              acc[a][b][4 * rg + 0] += dj.x * x[0];
+              acc[a][b][4 * rg + 1] += dj.y * x[1];
+              acc[a][b][4 * rg + 2] += dj.z * x[2];
+              acc[a][b][4 * rg + 3] += dj.w * x[3];
+            }
+          }
+        }
+      }
+    }
+  };
+
   // Ring of ST stages: stage kt lives in slot kt % ST.  Before computing
   // stage kt a wave waits until its own loads of stage kt are done (the
   // loads of the up to ST-2 later stages may stay in flight); the barrier
@@ -281,6 +361,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
     ring_barrier();
     if (kt + ST - 1 < nk) issue(kt + ST - 1, (kt + ST - 1) % ST);
     compute(kt % ST);
+    if (MODE != MODE_GRAM) capture(kt % ST, kt);
   }
   wait_vm_lgkm0<0>();
   __syncthreads();
@@ -290,8 +371,6 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
   //    BM x BN tile (rows padded by one chunk);
   // 2. direct store of tile rows; 3. transposed store (mirror / Xᵀ).
   T* O = reinterpret_cast<T*>(g.out) + (size_t)slice * g.o_bs;
-  const T* E = reinterpret_cast<const T*>(g.E) + (size_t)slice * g.e_bs;
-  const float* din = g.d_in + (size_t)slice * g.d_bs;
   float* dout = g.d_out + (size_t)slice * g.d_bs;
   const bool diag_tile = mode_is_tri(MODE) && ti == tj;
   T* S = reinterpret_cast<T*>(lds);
@@ -321,7 +400,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
           }
         } else if (MODE == MODE_POLY) {
           float o[4];
-          Quad<T>::unpack(*reinterpret_cast<const typename Quad<T>::Raw*>(E + (size_t)i * g.lde + j), o);
+          Quad<T>::unpack(obuf[a][b][rg], o);
           const float4 dj = *reinterpret_cast<const float4*>(din + j);
           const float dje[4] = {dj.x, dj.y, dj.z, dj.w};
           const float di = din[i];
@@ -334,19 +413,9 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
             }
           }
         } else {
-          float x[4];
-          Quad<T>::unpack(*reinterpret_cast<const typename Quad<T>::Raw*>(E + (size_t)i * g.lde + j), x);
-          if (MODE == MODE_UPD_ROW) {
-            const float di = din[i];
+          // d_C ⊙ X was added to the accumulators in the K loop
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = v[e] + di * x[e];
-          } else {
-            const float4 dj = *reinterpret_cast<const float4*>(din + j);
-            w[0] = v[0] + dj.x * x[0];
-            w[1] = v[1] + dj.y * x[1];
-            w[2] = v[2] + dj.z * x[2];
-            w[3] = v[3] + dj.w * x[3];
-          }
+          for (int e = 0; e < 4; ++e) w[e] = v[e];
         }
         *reinterpret_cast<typename Quad<T>::Raw*>(S + il * SROW + jl) = Quad<T>::pack(w);
       }
