@@ -188,15 +188,16 @@ int run_gram(const void* x, void* oa, float* da, const Plan& p, hipStream_t st) 
 }
 
 int run_poly(const void* oa, const float* da, void* oc, float* dc, const Plan& p, float a, float b,
-             float c, hipStream_t st) {
+             float c, hipStream_t st, const float* d_norm = nullptr) {
   ns::StageKind k;
-  const GemmArgs g = ns::poly_args(p, oa, da, oc, dc, a, b, c, &k);
+  const GemmArgs g = ns::poly_args(p, oa, da, oc, dc, a, b, c, &k, d_norm);
   return launch_stage(NS_KIND_POLY, "poly launch", p, g, k, st);
 }
 
-int run_update(const void* x, const void* oc, const float* dc, void* xo, const Plan& p, hipStream_t st) {
+int run_update(const void* x, const void* oc, const float* dc, void* xo, const Plan& p, hipStream_t st,
+               const float* d_norm = nullptr) {
   ns::StageKind k;
-  const GemmArgs g = ns::update_args(p, x, oc, dc, xo, &k);
+  const GemmArgs g = ns::update_args(p, x, oc, dc, xo, &k, d_norm);
   return launch_stage(NS_KIND_UPDATE, "update launch", p, g, k, st);
 }
 
@@ -256,13 +257,23 @@ int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows, int
   float* dc = reinterpret_cast<float*>(ws + p.off_dc);
   float* part = reinterpret_cast<float*>(ws + p.off_part);
 
-  auto buf = [&](int s) -> void* { return ns::iterate_in_out(ns_steps, s) ? out : xtmp; };
+  const bool fold = ns::fold_normalisation(ns_steps);
+  const bool copy_in = ns::input_copy_needed(ns_steps, in == out);
+  auto buf = [&](int s) -> const void* {
+    if (s == 0 && fold) return copy_in ? xtmp : in;
+    return ns::iterate_in_out(ns_steps, s) ? out : xtmp;
+  };
+  auto wbuf = [&](int s) -> void* { return ns::iterate_in_out(ns_steps, s) ? out : xtmp; };
 
-  if (int s = run_normalize(in, buf(0), nullptr, p, part, st)) return s;
+  if (!fold)
+    if (int s = run_normalize(in, wbuf(0), nullptr, p, part, st)) return s;
+  if (copy_in)  // out == in, odd steps: X_0 is a copy of the input (see ns_plan.h)
+    if (int s = check_hip(hipMemcpyAsync(xtmp, in, bytes, hipMemcpyDeviceToDevice, st), "input copy")) return s;
   for (int s = 1; s <= ns_steps; ++s) {
+    const float* dn = (fold && s == 1) ? da : nullptr;  // raw Gram diagonal -> ||x||_F
     if (int e = run_gram(buf(s - 1), oa, da, p, st)) return e;
-    if (int e = run_poly(oa, da, oc, dc, p, a, b, c, st)) return e;
-    if (int e = run_update(buf(s - 1), oc, dc, buf(s), p, st)) return e;
+    if (int e = run_poly(oa, da, oc, dc, p, a, b, c, st, dn)) return e;
+    if (int e = run_update(buf(s - 1), oc, dc, wbuf(s), p, st, dn)) return e;
   }
   record_config(p, ns_steps);
   return NS_OK;

@@ -93,6 +93,12 @@ __device__ __forceinline__ void mfma_chunk(f32x16& acc, uint4 a, uint4 b, float)
 
 // ------------------------------------------------------------- MFMA kernel
 
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer descriptor (gfx9 V#) over `bytes` bytes at `base`, stride 0: a load
@@ -272,6 +278,19 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
   // registers until the epilogue.
   typedef typename Quad<T>::Raw QRaw;
   const float* din = g.d_in + (size_t)slice * g.d_bs;
+
+  // 1 / (||x||_F + eps) from the raw Gram diagonal (first step only); every
+  // wave sums the slice's diagonal in the same order, so all agree bitwise
+  float inv_norm = 1.0f;
+  if (MODE != MODE_GRAM && g.d_norm != nullptr) {
+    const float* dn = g.d_norm + (size_t)slice * g.d_bs;
+    float t = 0.0f;
+    for (int i = lane; i < g.d_bs; i += 64) t += dn[i];
+    t = wave_sum(t);
+    inv_norm = 1.0f / (sqrtf(t) + g.eps);
+  }
+  const float cb = (MODE == MODE_POLY) ? g.cb * inv_norm * inv_norm : 0.0f;
+  const float cc = (MODE == MODE_POLY) ? g.cc * (inv_norm * inv_norm) * (inv_norm * inv_norm) : 0.0f;
   float drow[SM];
   QRaw obuf[MODE == MODE_POLY ? SM : 1][MODE == MODE_POLY ? SN : 1][4];
   if (MODE == MODE_UPD_ROW) {
@@ -406,16 +425,16 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
           const float di = din[i];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            w[e] = g.cb * o[e] + g.cc * (v[e] + (di + dje[e]) * o[e]);
+            w[e] = cb * o[e] + cc * (v[e] + (di + dje[e]) * o[e]);
             if (i == j + e) {
-              dout[i] = g.ca + g.cb * di + g.cc * (v[e] + di * di);
+              dout[i] = g.ca + cb * di + cc * (v[e] + di * di);
               w[e] = 0.0f;
             }
           }
         } else {
           // d_C ⊙ X was added to the accumulators in the K loop
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = v[e];
+          for (int e = 0; e < 4; ++e) w[e] = v[e] * inv_norm;
         }
         *reinterpret_cast<typename Quad<T>::Raw*>(S + il * SROW + jl) = Quad<T>::pack(w);
       }
@@ -461,12 +480,6 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
 }
 
 // --------------------------------------------------------- normalisation
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 
 __device__ __forceinline__ float sumsq16(uint4 u, bf16) {
   float s = 0.0f;

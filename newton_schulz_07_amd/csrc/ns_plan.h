@@ -59,7 +59,9 @@ inline Plan make_plan(int64_t batch, int64_t rows, int64_t cols, int dtype) {
 
 // The iterate X_s (s = 0 after normalisation) is held in `out` when
 // (steps - s) is even and in the workspace temporary otherwise, so the last
-// step writes `out` and no update reads the buffer it writes.
+// step writes `out` and no update reads the buffer it writes.  When the
+// normalisation is folded into the first step (fold_normalisation), X_0 is
+// the raw input itself.
 inline bool iterate_in_out(int steps, int s) { return ((steps - s) % 2) == 0; }
 
 inline NormArgs norm_args(const Plan& p, const void* x, void* y, float* norms, float* partials) {
@@ -108,7 +110,7 @@ inline GemmArgs gram_args(const Plan& p, const void* x, void* oa, float* da, Sta
 
 // C = a I + b A + c A A from the split A, written split the same way.
 inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* oc, float* dc, float a,
-                          float b, float c, StageKind* kind) {
+                          float b, float c, StageKind* kind, const float* d_norm = nullptr) {
   const TileCfg t = tile_cfg(p.dtype, true, plan_wide_tri(p));
   GemmArgs g{};
   g.P = g.Q = oa;
@@ -130,13 +132,15 @@ inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* 
   g.ca = a;
   g.cb = b;
   g.cc = c;
+  g.d_norm = d_norm;
+  g.eps = kNormEps;
   *kind = StageKind{MODE_POLY, false, false, plan_wide_tri(p)};
   return g;
 }
 
 // X' = C X (rows <= cols) or X C (rows > cols), C = O_C + diag(d_C).
 inline GemmArgs update_args(const Plan& p, const void* x, const void* oc, const float* dc, void* xo,
-                            StageKind* kind) {
+                            StageKind* kind, const float* d_norm = nullptr) {
   const TileCfg t = tile_cfg(p.dtype, false);
   GemmArgs g{};
   if (!p.tall) {  // P = rows of O_C, Q(j, k) = X[k][j] (natural layout)
@@ -173,7 +177,17 @@ inline GemmArgs update_args(const Plan& p, const void* x, const void* oc, const 
   g.d_in = dc;
   g.d_out = nullptr;
   g.d_bs = p.m;
+  g.d_norm = d_norm;
+  g.eps = kNormEps;
   return g;
 }
+
+// The first step runs on the raw input (normalisation folded into the first
+// poly and update, no separate passes) whenever there is a step.  When
+// out == in and the step count is odd, the first update would write `out`,
+// the input it still reads: the input is then first copied to the
+// temporary, which serves as X_0 (the result stays bitwise the same).
+inline bool fold_normalisation(int steps) { return steps >= 1; }
+inline bool input_copy_needed(int steps, bool out_is_in) { return steps >= 1 && out_is_in && (steps & 1); }
 
 }  // namespace ns

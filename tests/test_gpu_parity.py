@@ -90,13 +90,29 @@ def test_zero_slice_gives_zeros_and_scales_are_per_slice():
     assert rel_err(to64(y[[0, 2]]), ref[[0, 2]]).max() <= 1e-4
 
 
+@pytest.mark.parametrize("scale", [1e-4, 1e4])
+def test_unnormalised_magnitudes(scale):
+    # the first step works on the raw input and takes the norm from the trace
+    # of its Gram matrix: large and small magnitudes must not matter
+    dev = device()
+    x = gaussian((3, 136, 264), 725, torch.float32, scale=scale)
+    ref = newton_schulz_batched(x.double().numpy())
+    for steps in (1, 2, 5):
+        y = ns.orthogonalize(x.to(dev), steps=steps)
+        torch.cuda.synchronize()
+        assert rel_err(to64(y), newton_schulz_batched(x.double().numpy(), steps=steps)).max() <= 1e-4
+    yb = ns.orthogonalize(x.to(torch.bfloat16).to(dev))
+    torch.cuda.synchronize()
+    assert rel_err(to64(yb), ref).max() <= 1e-2
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_in_place(dtype):
     dev = device()
     x = gaussian((2, 136, 264), 730, dtype).to(dev)
     want = ns.orthogonalize(x.clone())
     ns.orthogonalize(x, out=x)
-    for steps in (0, 1, 4):
+    for steps in (0, 1, 2, 3, 4):
         z = gaussian((2, 136, 264), 731 + steps, dtype).to(dev)
         w = ns.orthogonalize(z.clone(), steps=steps)
         ns.orthogonalize(z, steps=steps, out=z)
@@ -144,11 +160,14 @@ def test_timing_records_each_launch():
     ns.ns_timing_reset()
     ns.ns_timing_enable(0x1f)
     try:
+        # with steps the normalisation rides in the first step (no separate
+        # passes); ns_steps = 0 runs the two normalisation passes only
         ns.orthogonalize(x, steps=3)
+        ns.orthogonalize(x, steps=0)
     finally:
         ns.ns_timing_enable(0)
     for kind, n in ((ns.NS_KIND_SUMSQ, 1), (ns.NS_KIND_SCALE, 1), (ns.NS_KIND_GRAM, 3),
                     (ns.NS_KIND_POLY, 3), (ns.NS_KIND_UPDATE, 3)):
         ms, cnt = ns.ns_timing_query(kind)
-        assert cnt == n and ms > 0
+        assert cnt == n and ms > 0, (kind, cnt)
     ns.ns_timing_reset()
