@@ -172,6 +172,7 @@ int run_normalize(const void* x, void* y, float* norms, const Plan& p, float* pa
   if (int s = check_hip(timed_launch(NS_KIND_SUMSQ, st, [&] { return ns::launch_sumsq(p.dtype, g, batch, st); }),
                         "sum-of-squares launch"))
     return s;
+  if (y == nullptr) return NS_OK;  // sums of squares only (folded normalisation)
   return check_hip(timed_launch(NS_KIND_SCALE, st, [&] { return ns::launch_scale(p.dtype, g, batch, st); }),
                    "scale launch");
 }
@@ -181,16 +182,16 @@ int launch_stage(int kind_id, const char* what, const Plan& p, const GemmArgs& g
   return check_hip(timed_launch(kind_id, st, [&] { return ns::launch_gemm(p.dtype, k, g, st); }), what);
 }
 
-int run_gram(const void* x, void* oa, float* da, const Plan& p, hipStream_t st) {
+int run_gram(const void* x, void* oa, float* da, const Plan& p, hipStream_t st, const float* d_norm = nullptr) {
   ns::StageKind k;
-  const GemmArgs g = ns::gram_args(p, x, oa, da, &k);
+  const GemmArgs g = ns::gram_args(p, x, oa, da, &k, d_norm);
   return launch_stage(NS_KIND_GRAM, "gram launch", p, g, k, st);
 }
 
 int run_poly(const void* oa, const float* da, void* oc, float* dc, const Plan& p, float a, float b,
-             float c, hipStream_t st, const float* d_norm = nullptr) {
+             float c, hipStream_t st) {
   ns::StageKind k;
-  const GemmArgs g = ns::poly_args(p, oa, da, oc, dc, a, b, c, &k, d_norm);
+  const GemmArgs g = ns::poly_args(p, oa, da, oc, dc, a, b, c, &k);
   return launch_stage(NS_KIND_POLY, "poly launch", p, g, k, st);
 }
 
@@ -205,11 +206,13 @@ void record_config(const Plan& p, int steps) {
   const ns::TileCfg tt = ns::tile_cfg(p.dtype, true, ns::plan_wide_tri(p)), tr = ns::tile_cfg(p.dtype, false);
   char buf[640];
   std::snprintf(buf, sizeof(buf),
-                "dtype=%s batch=%lld rows=%lld cols=%lld m=%lld %s steps=%d | norm: sumsq+scale (%lldx16B blocks) | "
+                "dtype=%s batch=%lld rows=%lld cols=%lld m=%lld %s steps=%d | norm: %s (%lldx16B blocks) | "
                 "mfma=%s | gram,poly: lower-tri tile=%dx%d waves=%dx%d k=%dB ring=%d gram-operands=%s | update: %s "
                 "tile=%dx%d waves=%dx%d k=%dB ring=%d X-operand=%s",
                 p.dtype == NS_DTYPE_BF16 ? "bf16" : "fp32", (long long)p.batch, (long long)p.rows,
-                (long long)p.cols, (long long)p.m, p.tall ? "tall" : "wide", steps, ns::kNormChunkVecs,
+                (long long)p.cols, (long long)p.m, p.tall ? "tall" : "wide", steps,
+                ns::fold_normalisation(steps) ? "sumsq, 1/||x|| folded into step 1" : "sumsq+scale",
+                ns::kNormChunkVecs,
                 p.dtype == NS_DTYPE_BF16 ? "32x32x16_bf16" : "32x32x2_f32", tt.bm, tt.bn, tt.wm, tt.wn,
                 tt.cpr * 16, tt.st, p.tall ? "columns(transposed-read)" : "rows", p.tall ? "X*C" : "C*X", tr.bm,
                 tr.bn, tr.wm, tr.wn, tr.cpr * 16, tr.st, p.tall ? "rows" : "columns(transposed-read)");
@@ -265,14 +268,14 @@ int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows, int
   };
   auto wbuf = [&](int s) -> void* { return ns::iterate_in_out(ns_steps, s) ? out : xtmp; };
 
-  if (!fold)
-    if (int s = run_normalize(in, wbuf(0), nullptr, p, part, st)) return s;
+  // folded: sums of squares only; otherwise (no step) X0 = x / (||x|| + eps)
+  if (int s = run_normalize(in, fold ? nullptr : wbuf(0), nullptr, p, part, st)) return s;
   if (copy_in)  // out == in, odd steps: X_0 is a copy of the input (see ns_plan.h)
     if (int s = check_hip(hipMemcpyAsync(xtmp, in, bytes, hipMemcpyDeviceToDevice, st), "input copy")) return s;
   for (int s = 1; s <= ns_steps; ++s) {
-    const float* dn = (fold && s == 1) ? da : nullptr;  // raw Gram diagonal -> ||x||_F
-    if (int e = run_gram(buf(s - 1), oa, da, p, st)) return e;
-    if (int e = run_poly(oa, da, oc, dc, p, a, b, c, st, dn)) return e;
+    const float* dn = (fold && s == 1) ? part : nullptr;  // partial sums of squares -> ||x||_F
+    if (int e = run_gram(buf(s - 1), oa, da, p, st, dn)) return e;
+    if (int e = run_poly(oa, da, oc, dc, p, a, b, c, st)) return e;
     if (int e = run_update(buf(s - 1), oc, dc, wbuf(s), p, st, dn)) return e;
   }
   record_config(p, ns_steps);

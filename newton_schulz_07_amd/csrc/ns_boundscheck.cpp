@@ -187,9 +187,10 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
       for (int wave = 0; wave < NW; ++wave)
         replay_dma(wave, NIW, t, es, kind.p_nat, kind.q_nat, kt * BK, g, slice, i0, j0, STAGE, kt % t.st, LDS, what);
     }
-    // norm folded into the first step: the raw Gram diagonal of the slice
-    if (mode != MODE_GRAM && g.d_norm != nullptr)
-      for (int i = 0; i < g.d_bs; ++i) access(g.d_norm, ((long long)slice * g.d_bs + i) * 4, 4, what);
+    // norm folded into the first step: the slice's partial sums of squares
+    if (mode != MODE_POLY && g.d_norm != nullptr)
+      for (int i = 0; i < g.norm_n; ++i) access(g.d_norm, ((long long)slice * g.norm_n + i) * 4, 4, what);
+    if (mode == MODE_POLY && g.d_norm != nullptr) fail(std::string(what) + ": poly takes no norm");
     // epilogue operands captured from the K stages (mirrors capture())
     const long long db0 = (long long)slice * g.d_bs;
     const int RCQ = t.bn / EPC;
@@ -353,19 +354,19 @@ void replay_call(int dtype, long long batch, long long rows, long long cols, int
   const bool copy_in = input_copy_needed(steps, alias);
   auto wbuf = [&](int s) -> void* { return iterate_in_out(steps, s) ? out : xtmp; };
   auto buf = [&](int s) -> void* { return (s == 0 && fold) ? (copy_in ? xtmp : in) : wbuf(s); };
-  if (!fold) {
-    const NormArgs ng = norm_args(p, in, wbuf(0), nullptr, part);
+  {
+    const NormArgs ng = norm_args(p, in, fold ? nullptr : wbuf(0), nullptr, part);
     replay_norm(ng, (int)batch, false, "sumsq");
-    replay_norm(ng, (int)batch, true, "scale");
+    if (!fold) replay_norm(ng, (int)batch, true, "scale");
   }
   const bool cov = (long long)batch * std::max<long long>(p.m * p.m, rows * cols) <= 80LL * 1000 * 1000;
   for (int s = 1; s <= steps; ++s) {
     if (s != 1 && s != steps && s != 2) continue;  // later steps differ only in which buffer is which
-    const float* dn = (fold && s == 1) ? da : nullptr;
+    const float* dn = (fold && s == 1) ? part : nullptr;
     StageKind kind;
-    GemmArgs g = gram_args(p, buf(s - 1), oa, da, &kind);
+    GemmArgs g = gram_args(p, buf(s - 1), oa, da, &kind, dn);
     replay_gemm(g, kind, dtype, cov, "gram");
-    g = poly_args(p, oa, da, oc, dc, 3.4445f, -4.775f, 2.0315f, &kind, dn);
+    g = poly_args(p, oa, da, oc, dc, 3.4445f, -4.775f, 2.0315f, &kind);
     replay_gemm(g, kind, dtype, cov, "poly");
     if (buf(s - 1) == wbuf(s)) fail("update reads the buffer it writes");
     g = update_args(p, buf(s - 1), oc, dc, wbuf(s), &kind, dn);

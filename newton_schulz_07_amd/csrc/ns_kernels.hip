@@ -279,18 +279,19 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
   typedef typename Quad<T>::Raw QRaw;
   const float* din = g.d_in + (size_t)slice * g.d_bs;
 
-  // 1 / (||x||_F + eps) from the raw Gram diagonal (first step only); every
-  // wave sums the slice's diagonal in the same order, so all agree bitwise
+  // 1 / (||x||_F + eps) from the slice's partial sums of squares (first
+  // step only); every wave of every kernel sums them in the same order, so
+  // the Gram and the update agree bitwise
   float inv_norm = 1.0f;
-  if (MODE != MODE_GRAM && g.d_norm != nullptr) {
-    const float* dn = g.d_norm + (size_t)slice * g.d_bs;
+  if (MODE != MODE_POLY && g.d_norm != nullptr) {
+    const float* dn = g.d_norm + (size_t)slice * g.norm_n;
     float t = 0.0f;
-    for (int i = lane; i < g.d_bs; i += 64) t += dn[i];
+    for (int i = lane; i < g.norm_n; i += 64) t += dn[i];
     t = wave_sum(t);
     inv_norm = 1.0f / (sqrtf(t) + g.eps);
   }
-  const float cb = (MODE == MODE_POLY) ? g.cb * inv_norm * inv_norm : 0.0f;
-  const float cc = (MODE == MODE_POLY) ? g.cc * (inv_norm * inv_norm) * (inv_norm * inv_norm) : 0.0f;
+  const float gram_scale = inv_norm * inv_norm;
+  const float cb = g.cb, cc = g.cc;
   float drow[SM];
   QRaw obuf[MODE == MODE_POLY ? SM : 1][MODE == MODE_POLY ? SN : 1][4];
   if (MODE == MODE_UPD_ROW) {
@@ -411,9 +412,9 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
         if (MODE == MODE_GRAM) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            w[e] = v[e];
+            w[e] = v[e] * gram_scale;
             if (i == j + e) {
-              dout[i] = v[e];
+              dout[i] = w[e];
               w[e] = 0.0f;
             }
           }

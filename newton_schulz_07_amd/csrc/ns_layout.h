@@ -204,11 +204,13 @@ struct GemmArgs {
   float* d_out;       // diagonal vector written (Gram: d_A, poly: d_C)
   long long d_bs;     // slice stride of both diagonal vectors
   float ca, cb, cc;   // quintic coefficients (poly only)
-  // First step on an unnormalised input: d_norm is the diagonal of the Gram
-  // of the raw input, whose sum is ||x||_F^2.  With inv = 1 / (||x||_F + eps)
-  // the poly uses b inv^2 and c inv^4 (A = inv^2 A_raw) and the update
-  // scales its result by inv (X0 = inv x).  Null: the input is already X_s.
+  // First step on an unnormalised input: d_norm holds the slice's partial
+  // sums of squares of the raw input (norm_n per slice), whose total is
+  // ||x||_F^2.  With inv = 1 / (||x||_F + eps) the Gram scales its result by
+  // inv^2 (A of X0 = inv x) and the update scales its result by inv, so X0 is
+  // never formed.  Null: the operands already are X_s.
   const float* d_norm;
+  int norm_n;
   float eps;
 };
 

@@ -88,7 +88,8 @@ inline bool plan_wide_tri(const Plan& p) { return use_wide_tri(p.dtype, p.batch,
 
 // A = X Xᵀ (rows <= cols: rows of X are K-contiguous) or Xᵀ X (rows > cols:
 // columns of X, read in X's natural layout), mirrored into one m x m matrix.
-inline GemmArgs gram_args(const Plan& p, const void* x, void* oa, float* da, StageKind* kind) {
+inline GemmArgs gram_args(const Plan& p, const void* x, void* oa, float* da, StageKind* kind,
+                          const float* d_norm = nullptr) {
   const TileCfg t = tile_cfg(p.dtype, true, plan_wide_tri(p));
   GemmArgs g{};
   g.P = g.Q = x;
@@ -104,13 +105,16 @@ inline GemmArgs gram_args(const Plan& p, const void* x, void* oa, float* da, Sta
   g.ldo = g.ldt = (int)p.m;
   g.d_out = da;
   g.d_bs = p.m;
+  g.d_norm = d_norm;
+  g.norm_n = p.norm_chunks;
+  g.eps = kNormEps;
   *kind = StageKind{MODE_GRAM, p.tall, p.tall, plan_wide_tri(p)};
   return g;
 }
 
 // C = a I + b A + c A A from the split A, written split the same way.
 inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* oc, float* dc, float a,
-                          float b, float c, StageKind* kind, const float* d_norm = nullptr) {
+                          float b, float c, StageKind* kind) {
   const TileCfg t = tile_cfg(p.dtype, true, plan_wide_tri(p));
   GemmArgs g{};
   g.P = g.Q = oa;
@@ -132,8 +136,6 @@ inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* 
   g.ca = a;
   g.cb = b;
   g.cc = c;
-  g.d_norm = d_norm;
-  g.eps = kNormEps;
   *kind = StageKind{MODE_POLY, false, false, plan_wide_tri(p)};
   return g;
 }
@@ -178,15 +180,19 @@ inline GemmArgs update_args(const Plan& p, const void* x, const void* oc, const 
   g.d_out = nullptr;
   g.d_bs = p.m;
   g.d_norm = d_norm;
+  g.norm_n = p.norm_chunks;
   g.eps = kNormEps;
   return g;
 }
 
-// The first step runs on the raw input (normalisation folded into the first
-// poly and update, no separate passes) whenever there is a step.  When
-// out == in and the step count is odd, the first update would write `out`,
-// the input it still reads: the input is then first copied to the
-// temporary, which serves as X_0 (the result stays bitwise the same).
+// Whenever there is a step, the first step runs on the raw input: one
+// sum-of-squares pass gives ||x||_F, the first Gram scales A by 1/||x||^2 and
+// the first update scales X_1 by 1/||x|| (X0 = x/||x|| is never written).
+// Every product that sees raw values is then X Xᵀ, whose range is that of the
+// sum of squares itself.  When out == in and the step count is odd, the first
+// update would write `out`, the input it still reads: the input is then first
+// copied to the temporary, which serves as X_0 (the result stays bitwise the
+// same).
 inline bool fold_normalisation(int steps) { return steps >= 1; }
 inline bool input_copy_needed(int steps, bool out_is_in) { return steps >= 1 && out_is_in && (steps & 1); }
 

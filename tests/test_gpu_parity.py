@@ -90,10 +90,12 @@ def test_zero_slice_gives_zeros_and_scales_are_per_slice():
     assert rel_err(to64(y[[0, 2]]), ref[[0, 2]]).max() <= 1e-4
 
 
-@pytest.mark.parametrize("scale", [1e-4, 1e4])
+@pytest.mark.parametrize("scale", [1e-12, 1e-4, 1e4, 1e12])
 def test_unnormalised_magnitudes(scale):
-    # the first step works on the raw input and takes the norm from the trace
-    # of its Gram matrix: large and small magnitudes must not matter
+    # the first Gram works on the raw input and scales its result by
+    # 1/||x||^2: magnitudes must not matter, up to ||x||^4 far beyond fp32
+    # (1e12 entries here), where a product of two raw Gram matrices would
+    # overflow
     dev = device()
     x = gaussian((3, 136, 264), 725, torch.float32, scale=scale)
     ref = newton_schulz_batched(x.double().numpy())
@@ -160,13 +162,14 @@ def test_timing_records_each_launch():
     ns.ns_timing_reset()
     ns.ns_timing_enable(0x1f)
     try:
-        # with steps the normalisation rides in the first step (no separate
-        # passes); ns_steps = 0 runs the two normalisation passes only
+        # with steps only the sum of squares runs before the first step (the
+        # scaling rides in the first Gram and update); ns_steps = 0 runs the
+        # two normalisation passes only
         ns.orthogonalize(x, steps=3)
         ns.orthogonalize(x, steps=0)
     finally:
         ns.ns_timing_enable(0)
-    for kind, n in ((ns.NS_KIND_SUMSQ, 1), (ns.NS_KIND_SCALE, 1), (ns.NS_KIND_GRAM, 3),
+    for kind, n in ((ns.NS_KIND_SUMSQ, 2), (ns.NS_KIND_SCALE, 1), (ns.NS_KIND_GRAM, 3),
                     (ns.NS_KIND_POLY, 3), (ns.NS_KIND_UPDATE, 3)):
         ms, cnt = ns.ns_timing_query(kind)
         assert cnt == n and ms > 0, (kind, cnt)
