@@ -84,47 +84,75 @@ void replay_dma(int wave, int niw, const TileCfg& t, int es, bool pnat, bool qna
       const bool nat = d.is_p ? pnat : qnat;
       const int ld = d.is_p ? g.ldp : g.ldq;
       const int g_row = (d.is_p ? i0 : j0) + d.row;
-      const bool ok = g_row < (d.is_p ? g.M : g.N) && k0 + d.kpos < g.K;
+      const bool row_ok = g_row < (d.is_p ? g.M : g.N);
+      const bool ok = row_ok && k0 + d.kpos < g.K;
       if (d.row < 0 || d.row >= (d.is_p ? t.bm : t.bn) || d.kpos < 0 || d.kpos >= t.cpr * EPC)
         fail(std::string(what) + ": loader index outside the tile");
-      if (!ok) continue;  // offset kOut: reads zeros
-      const long long off = nat ? ((long long)(k0 + d.kpos) * ld + g_row) * es : ((long long)g_row * ld + k0 + d.kpos) * es;
-      if (off + 16 > (d.is_p ? pbytes : qbytes) || off >= (long long)kOut)
+      // the offset exactly as issue() forms it (32-bit unsigned arithmetic)
+      const int BK = t.cpr * EPC, kt = k0 / BK;
+      const unsigned src_off = row_ok ? (unsigned)(nat ? ((long long)d.kpos * ld + g_row) * es
+                                                       : ((long long)g_row * ld + d.kpos) * es)
+                                      : kOut;
+      const unsigned step = nat ? (unsigned)(BK * ld * es) : (unsigned)(BK * es);
+      const unsigned long long run = (unsigned long long)src_off + (unsigned long long)kt * step;
+      if (run >= (1ull << 32)) fail(std::string(what) + ": DMA offset wraps 32 bits");
+      const bool full = k0 + BK <= g.K;
+      const unsigned off = (full || k0 + d.kpos < g.K) ? (unsigned)run : kOut;
+      const long long range = d.is_p ? pbytes : qbytes;
+      if (!ok) {
+        if ((long long)off < range) fail(std::string(what) + ": zero-fill lane reads inside the slice");
+        continue;  // past the range check: reads zeros
+      }
+      const long long want = nat ? ((long long)(k0 + d.kpos) * ld + g_row) * es : ((long long)g_row * ld + k0 + d.kpos) * es;
+      if ((long long)off != want) fail(std::string(what) + ": DMA offset differs from the element's");
+      if (want + 16 > range || want >= (long long)kOut)
         fail(std::string(what) + ": in-range load past the slice");
-      access(d.is_p ? g.P : g.Q, (long long)slice * (d.is_p ? g.p_bs : g.q_bs) * es + off, 16, what);
+      access(d.is_p ? g.P : g.Q, (long long)slice * (d.is_p ? g.p_bs : g.q_bs) * es + want, 16, what);
     }
   }
 }
 
-// Fragment reads of one operand region (mirrors compute()/nat_frag): every
-// LDS byte read lies inside the region.
+// Fragment reads of one operand region (mirrors load_step()/nat_frag): the
+// kernel reads per-lane bases plus compile-time offsets (kc_lane_byte,
+// nat_lane_byte_*).  Every such byte address must equal the address of the
+// element the DMA layout (lds_swz / nat_swz) puts there, and lie inside the
+// region.
 void replay_frag_reads(const TileCfg& t, int es, bool nat, int rows_region, int wave_rows, int nblk, int wofs,
                        const char* what) {
   const int EPC = 16 / es, rc = rows_region / EPC, region = rows_region * t.cpr;
+  const int nh = es == 2 ? 2 : 4;
+  if (t.cpr != 4 && t.cpr != 8) fail(std::string(what) + ": fragment addressing needs 4 or 8 chunks per row");
   for (int lane = 0; lane < 64; ++lane)
     for (int s = 0; s < t.cpr / 2; ++s)
       for (int a = 0; a < nblk; ++a) {
         const int rb = wofs + a * 32;
         if (!nat) {
-          lds_index(lds_swz(rb + (lane & 31), 2 * s + (lane >> 5), t.cpr), region, what);
+          const int got = kc_lane_byte(wofs, s ^ kc_sigma(a, t.cpr), lane, t.cpr) + a * 32 * t.cpr * 16;
+          const int want = lds_swz(rb + (lane & 31), 2 * s + (lane >> 5), t.cpr) * 16;
+          if (got != want) fail(std::string(what) + ": K-contiguous fragment base + offset != swizzled chunk");
+          lds_index(got / 16, region, what);
           continue;
         }
-        if (es == 2) {
-          for (int h = 0; h < 2; ++h) {
-            const int kr = nat_tr_kr(s, h, lane), col = nat_tr_col(rb, lane);
-            if (kr >= t.cpr * EPC || col + 3 >= rows_region) fail(std::string(what) + ": transposed read outside tile");
-            const int c = (col >> 3) ^ nat_swz(kr, rc, es);
-            if (c >= rc) fail(std::string(what) + ": swizzled chunk past the row");
-            lds_index(kr * rc + c, region, what);
+        for (int h = 0; h < nh; ++h) {
+          const int got = (es == 2 ? nat_lane_byte_bf16(rb, h, lane, rc) : nat_lane_byte_f32(rb, h, lane, rc)) +
+                          s * nat_step_bytes(rc, es);
+          int kr, col, c, want;
+          if (es == 2) {
+            kr = nat_tr_kr(s, h, lane);
+            col = nat_tr_col(rb, lane);
+            if (col + 3 >= rows_region) fail(std::string(what) + ": transposed read outside tile");
+            c = (col >> 3) ^ nat_swz(kr, rc, es);
+            want = (kr * rc + c) * 16 + (col & 7) * 2;
+          } else {
+            kr = 8 * s + 4 * (lane >> 5) + h;
+            col = rb + (lane & 31);
+            c = (col >> 2) ^ nat_swz(kr, rc, es);
+            want = (kr * rc + c) * 16 + (col & 3) * 4;
           }
-        } else {
-          const int col = rb + (lane & 31);
-          for (int e = 0; e < 4; ++e) {
-            const int kr = 8 * s + 4 * (lane >> 5) + e;
-            const int c = (col >> 2) ^ nat_swz(kr, rc, es);
-            if (kr >= t.cpr * EPC || c >= rc) fail(std::string(what) + ": fp32 natural read outside tile");
-            lds_index(kr * rc + c, region, what);
-          }
+          if (kr >= t.cpr * EPC) fail(std::string(what) + ": natural read past the stage's k rows");
+          if (c >= rc) fail(std::string(what) + ": swizzled chunk past the row");
+          if (got != want) fail(std::string(what) + ": natural fragment base + offset != swizzled element");
+          lds_index(got / 16, region, what);
         }
       }
   (void)wave_rows;

@@ -29,6 +29,10 @@
 #include "ns_layout.h"
 #include "ns_plan.h"
 
+#ifndef NS_FRAG_BARRIER
+#define NS_FRAG_BARRIER 1
+#endif
+
 namespace ns {
 
 typedef __bf16 bf16;
@@ -142,31 +146,31 @@ __device__ __forceinline__ void ring_barrier() {
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // One MFMA operand fragment (8 bf16 or 4 fp32 k values of one tile row, the
-// same k assignment as a K-contiguous chunk) from a NAT tile in LDS.
-__device__ __forceinline__ uint4 nat_frag(const uint4* tile, int rc, int s, int rb, int lane, bf16) {
+// same k assignment as a K-contiguous chunk) from a NAT tile in LDS: `step`
+// addresses the step's k rows, off[] holds the lane's byte offsets of its
+// reads (nat_lane_byte_bf16 / _f32).
+__device__ __forceinline__ uint4 nat_frag(const char* step, const int* off, bf16) {
   uint32_t w[4];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int kr = nat_tr_kr(s, h, lane), col = nat_tr_col(rb, lane);
-    const int pos = kr * rc + ((col >> 3) ^ nat_swz(kr, rc, 2));
-    const short* src = reinterpret_cast<const short*>(tile + pos) + (col & 7);
+    const short* src = reinterpret_cast<const short*>(step + off[h]);
     const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)src);
     w[2 * h] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
     w[2 * h + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
-__device__ __forceinline__ uint4 nat_frag(const uint4* tile, int rc, int s, int rb, int lane, float) {
-  // k = 8 s + 4 (lane / 32) + e, column rb + lane % 32
-  const int col = rb + (lane & 31);
+__device__ __forceinline__ uint4 nat_frag(const char* step, const int* off, float) {
   uint32_t w[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int kr = 8 * s + 4 * (lane >> 5) + e;
-    const int pos = kr * rc + ((col >> 2) ^ nat_swz(kr, rc, 4));
-    w[e] = reinterpret_cast<const uint32_t*>(tile + pos)[col & 3];
-  }
+  for (int e = 0; e < 4; ++e) w[e] = *reinterpret_cast<const uint32_t*>(step + off[e]);
   return make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ int nat_lane_byte(int rb, int h, int lane, int rc, bf16) {
+  return nat_lane_byte_bf16(rb, h, lane, rc);
+}
+__device__ __forceinline__ int nat_lane_byte(int rb, int h, int lane, int rc, float) {
+  return nat_lane_byte_f32(rb, h, lane, rc);
 }
 
 template <typename T, int BM, int BN, int WM, int WN, int CPR, int ST, int OCC, int MODE, bool PNAT, bool QNAT>
@@ -210,11 +214,10 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
   const i32x4 rQ = make_rsrc(Qbase, (unsigned)(g.q_bs * ES));
   constexpr unsigned kOutOfRange = 0x80000000u;
 
-  // per-lane source of each of this wave's load instructions: byte offset at
-  // k0 = 0, k position within the stage (>= K means zero fill), and the
-  // byte step from one stage to the next
-  unsigned src_off[NIW], src_step[NIW];
-  int src_k[NIW];
+  // Per-lane source of each of this wave's load instructions: the byte
+  // offset at k0 = 0 (past the slice end for rows past M / N).  From one
+  // stage to the next an operand's offsets move by a wave-uniform step.
+  unsigned src_off[NIW];
 #pragma unroll
   for (int t = 0; t < NIW; ++t) {
     const DmaSrc d = dma_src(wave * NIW + t, lane, BM, BN, CPR, EPC, PNAT, QNAT, ES);
@@ -224,17 +227,33 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
     const bool ok = g_row < (d.is_p ? g.M : g.N);
     const size_t off = nat ? ((size_t)d.kpos * ld + g_row) * ES : ((size_t)g_row * ld + d.kpos) * ES;
     src_off[t] = ok ? (unsigned)off : kOutOfRange;
-    src_k[t] = ok ? d.kpos : g.K;
-    src_step[t] = nat ? (unsigned)(BK * ld * ES) : (unsigned)(BK * ES);
   }
+  const unsigned step_p = PNAT ? (unsigned)(BK * g.ldp * ES) : (unsigned)(BK * ES);
+  const unsigned step_q = QNAT ? (unsigned)(BK * g.ldq * ES) : (unsigned)(BK * ES);
+  // Loads of stage kt into ring slot `slot`.  When the whole stage lies
+  // inside K (always, for K a multiple of BK) only rows past M / N need the
+  // zero fill, and their offset already starts past the slice end; otherwise
+  // each lane also checks its own k position.
   auto issue = [&](int kt, int slot) {
     const int k0 = kt * BK;
+    if (k0 + BK <= g.K) {
 #pragma unroll
-    for (int t = 0; t < NIW; ++t) {
-      const int idx = wave * NIW + t;  // wave-uniform
-      const unsigned off = (k0 + src_k[t] < g.K) ? src_off[t] + (unsigned)kt * src_step[t] : kOutOfRange;
-      const unsigned dst = lds_addr(lds + slot * STAGE + idx * 64);
-      dma16(dst, off, idx * 64 < LP ? rP : rQ);
+      for (int t = 0; t < NIW; ++t) {
+        const int idx = wave * NIW + t;  // wave-uniform
+        const bool is_p = idx * 64 < LP;
+        dma16(lds_addr(lds + slot * STAGE + idx * 64), src_off[t] + (unsigned)kt * (is_p ? step_p : step_q),
+              is_p ? rP : rQ);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NIW; ++t) {
+        const int idx = wave * NIW + t;
+        const bool is_p = idx * 64 < LP;
+        const int kpos = dma_src(idx, lane, BM, BN, CPR, EPC, PNAT, QNAT, ES).kpos;
+        const unsigned off =
+            (k0 + kpos < g.K) ? src_off[t] + (unsigned)kt * (is_p ? step_p : step_q) : kOutOfRange;
+        dma16(lds_addr(lds + slot * STAGE + idx * 64), off, is_p ? rP : rQ);
+      }
     }
   };
 
@@ -246,26 +265,62 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  const int half = lane >> 5, l32 = lane & 31;
+  const int l32 = lane & 31;
+
+  // Per-lane byte offsets of the fragment reads; every read of the K loop is
+  // one of them plus a compile-time offset (kc_lane_byte, nat_lane_byte_*).
+  constexpr int KS = CPR / 2;                      // MFMA k steps per stage
+  constexpr int NH = sizeof(T) == 2 ? 2 : 4;       // LDS reads per NAT fragment
+  constexpr int QOFF = LP * 16;                    // Q region within a stage
+  constexpr int NSP = nat_step_bytes(RCP, ES), NSQ = nat_step_bytes(RCQ, ES);
+  static_assert(CPR == 4 || CPR == 8, "fragment addressing assumes 4 or 8 chunks per row");
+  int kcp[PNAT ? 1 : KS], kcq[QNAT ? 1 : KS];
+  int natp[PNAT ? SM : 1][NH], natq[QNAT ? SN : 1][NH];
+  if constexpr (!PNAT) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kcp[s] = kc_lane_byte(wm * WTM, s, lane, CPR);
+  } else {
+#pragma unroll
+    for (int a = 0; a < SM; ++a)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) natp[a][h] = nat_lane_byte(wm * WTM + 32 * a, h, lane, RCP, T());
+  }
+  if constexpr (!QNAT) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kcq[s] = kc_lane_byte(wn * WTN, s, lane, CPR) + QOFF;
+  } else {
+#pragma unroll
+    for (int b = 0; b < SN; ++b)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) natq[b][h] = nat_lane_byte(wn * WTN + 32 * b, h, lane, RCQ, T()) + QOFF;
+  }
+  const char* lb = reinterpret_cast<const char*>(lds);
+  auto load_step = [&](int slot, int s, uint4 (&pf)[SM], uint4 (&qf)[SN]) {
+    const char* st = lb + slot * STAGE * 16;
+#pragma unroll
+    for (int a = 0; a < SM; ++a) {
+      if constexpr (PNAT) pf[a] = nat_frag(st + s * NSP, natp[a], T());
+      else pf[a] = *reinterpret_cast<const uint4*>(st + kcp[s ^ kc_sigma(a, CPR)] + a * 32 * CPR * 16);
+    }
+#pragma unroll
+    for (int b = 0; b < SN; ++b) {
+      if constexpr (QNAT) qf[b] = nat_frag(st + s * NSQ, natq[b], T());
+      else qf[b] = *reinterpret_cast<const uint4*>(st + kcq[s ^ kc_sigma(b, CPR)] + b * 32 * CPR * 16);
+    }
+  };
+  // fragments of step s + 1 are read while the MFMAs of step s run
   auto compute = [&](int slot) {
-    const uint4* Ps = lds + slot * STAGE;
-    const uint4* Qs = Ps + LP;
+    uint4 pf[2][SM], qf[2][SN];
+    load_step(slot, 0, pf[0], qf[0]);
 #pragma unroll
-    for (int s = 0; s < CPR / 2; ++s) {
-      const int ch = 2 * s + half;
-      uint4 pf[SM], qf[SN];
-#pragma unroll
-      for (int a = 0; a < SM; ++a)
-        pf[a] = PNAT ? nat_frag(Ps, RCP, s, wm * WTM + a * 32, lane, T())
-                     : Ps[lds_swz(wm * WTM + a * 32 + l32, ch, CPR)];
-#pragma unroll
-      for (int b = 0; b < SN; ++b)
-        qf[b] = QNAT ? nat_frag(Qs, RCQ, s, wn * WTN + b * 32, lane, T())
-                     : Qs[lds_swz(wn * WTN + b * 32 + l32, ch, CPR)];
+    for (int s = 0; s < KS; ++s) {
+      if (s + 1 < KS) load_step(slot, s + 1, pf[(s + 1) & 1], qf[(s + 1) & 1]);
+      // keep the scheduler from sinking these reads back to their uses
+      if (NS_FRAG_BARRIER) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int a = 0; a < SM; ++a)
 #pragma unroll
-        for (int b = 0; b < SN; ++b) mfma_chunk(acc[a][b], qf[b], pf[a], T());
+        for (int b = 0; b < SN; ++b) mfma_chunk(acc[a][b], qf[s & 1][b], pf[s & 1][a], T());
     }
   };
 
@@ -368,21 +423,31 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
   // loads of the up to ST-2 later stages may stay in flight); the barrier
   // then publishes every wave's part, and also certifies that slot
   // (kt-1) % ST is no longer read, so stage kt+ST-1 can be loaded into it.
+  // The loop runs in groups of ST stages (then a tail of fewer) so that every
+  // slot index, and with it every LDS address, is a compile-time constant.
   const int nk = (g.K + BK - 1) / BK;
-#pragma unroll
-  for (int s = 0; s < ST - 1; ++s)
-    if (s < nk) issue(s, s);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int after = nk - 1 - kt;  // stages issued after kt, capped at ST-2
+  auto stage = [&](int kt, int u) {  // u == kt % ST
+    const int after = nk - 1 - kt;   // stages issued after kt, capped at ST-2
     if (after >= ST - 2) wait_vm_lgkm0<NIW * (ST - 2)>();
     else if (ST > 3 && after == 2) wait_vm_lgkm0<NIW * 2>();
     else if (ST > 2 && after == 1) wait_vm_lgkm0<NIW>();
     else wait_vm_lgkm0<0>();
     ring_barrier();
-    if (kt + ST - 1 < nk) issue(kt + ST - 1, (kt + ST - 1) % ST);
-    compute(kt % ST);
-    if (MODE != MODE_GRAM) capture(kt % ST, kt);
+    if (kt + ST - 1 < nk) issue(kt + ST - 1, (u + ST - 1) % ST);
+    compute(u);
+    if (MODE != MODE_GRAM) capture(u, kt);
+  };
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nk) issue(s, s);
+  int kt0 = 0;
+  for (; kt0 + ST <= nk; kt0 += ST) {
+#pragma unroll
+    for (int u = 0; u < ST; ++u) stage(kt0 + u, u);
   }
+#pragma unroll
+  for (int u = 0; u < ST - 1; ++u)
+    if (kt0 + u < nk) stage(kt0 + u, u);
   wait_vm_lgkm0<0>();
   __syncthreads();
 

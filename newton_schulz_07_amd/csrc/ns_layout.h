@@ -171,6 +171,33 @@ NS_HD DmaSrc dma_src(int idx, int lane, int bm, int bn, int cpr, int epc, bool p
 NS_HD int nat_tr_kr(int s, int h, int lane) { return 16 * s + 8 * (lane >> 5) + 4 * h + ((lane & 15) >> 2); }
 NS_HD int nat_tr_col(int rb, int lane) { return rb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3); }
 
+// Fragment reads as a per-lane base plus a compile-time offset (LDS bytes
+// within one operand region of a stage), so that the K loop spends no VALU
+// work on addresses.
+//  K-contiguous: step s of block a (rows w0 + 32 a + lane % 32, chunk
+//  2 s + lane / 32; w0 a multiple of 32) reads
+//    kc_lane_byte(w0, s ^ kc_sigma(a, cpr), lane, cpr) + 32 a cpr 16.
+//  Rows 32 apart differ in their swizzle only in bit 2 of the chunk (cpr 8)
+//  or not at all (cpr 4), and flipping bit 2 of chunk 2 s + h is s ^ 2.
+NS_HD int kc_lane_byte(int w0, int s, int lane, int cpr) {
+  return lds_swz(w0 + (lane & 31), 2 * s + (lane >> 5), cpr) * 16;
+}
+NS_HD constexpr int kc_sigma(int a, int cpr) { return cpr == 8 ? 2 * (a & 1) : 0; }
+//  NAT bf16: read h of step s of the block at column rb reads
+//    nat_lane_byte_bf16(rb, h, lane, rc) + 16 s rc 16
+//  (a step moves the k row by 16, and nat_swz does not see that move).
+NS_HD int nat_lane_byte_bf16(int rb, int h, int lane, int rc) {
+  const int kr = nat_tr_kr(0, h, lane), col = nat_tr_col(rb, lane);
+  return (kr * rc + ((col >> 3) ^ nat_swz(kr, rc, 2))) * 16 + (col & 7) * 2;
+}
+//  NAT fp32: element e (k row 8 s + 4 (lane / 32) + e, column rb + lane % 32)
+//  reads nat_lane_byte_f32(rb, e, lane, rc) + 8 s rc 16.
+NS_HD int nat_lane_byte_f32(int rb, int e, int lane, int rc) {
+  const int kr = 4 * (lane >> 5) + e, col = rb + (lane & 31);
+  return (kr * rc + ((col >> 2) ^ nat_swz(kr, rc, 4))) * 16 + (col & 3) * 4;
+}
+NS_HD constexpr int nat_step_bytes(int rc, int esize) { return (esize == 2 ? 16 : 8) * rc * 16; }
+
 // MFMA operand roles: the A operand is the Q tile (output column j), the B
 // operand the P tile (output row i).  Register r of lane l of a 32x32 block
 // then holds row i = l % 32 and column j = 8 (r / 4) + 4 (l / 32) + r % 4,
