@@ -203,19 +203,21 @@ int run_update(const void* x, const void* oc, const float* dc, void* xo, const P
 }
 
 void record_config(const Plan& p, int steps) {
-  const ns::TileCfg tt = ns::tile_cfg(p.dtype, true, ns::plan_wide_tri(p)), tr = ns::tile_cfg(p.dtype, false);
-  char buf[640];
+  const ns::TileCfg tg = ns::tile_cfg(p.dtype, true, ns::plan_tri_class(p, true));
+  const ns::TileCfg tp = ns::tile_cfg(p.dtype, true, ns::plan_tri_class(p, false));
+  const ns::TileCfg tr = ns::tile_cfg(p.dtype, false);
+  char buf[768];
   std::snprintf(buf, sizeof(buf),
                 "dtype=%s batch=%lld rows=%lld cols=%lld m=%lld %s steps=%d | norm: %s (%lldx16B blocks) | "
-                "mfma=%s | gram,poly: lower-tri tile=%dx%d waves=%dx%d k=%dB ring=%d gram-operands=%s | update: %s "
-                "tile=%dx%d waves=%dx%d k=%dB ring=%d X-operand=%s",
+                "mfma=%s | gram: lower-tri tile=%dx%d waves=%dx%d k=%dB ring=%d operands=%s | poly: lower-tri "
+                "tile=%dx%d waves=%dx%d k=%dB ring=%d | update: %s tile=%dx%d waves=%dx%d k=%dB ring=%d X-operand=%s",
                 p.dtype == NS_DTYPE_BF16 ? "bf16" : "fp32", (long long)p.batch, (long long)p.rows,
                 (long long)p.cols, (long long)p.m, p.tall ? "tall" : "wide", steps,
                 ns::fold_normalisation(steps) ? "sumsq, 1/||x|| folded into step 1" : "sumsq+scale",
-                ns::kNormChunkVecs,
-                p.dtype == NS_DTYPE_BF16 ? "32x32x16_bf16" : "32x32x2_f32", tt.bm, tt.bn, tt.wm, tt.wn,
-                tt.cpr * 16, tt.st, p.tall ? "columns(transposed-read)" : "rows", p.tall ? "X*C" : "C*X", tr.bm,
-                tr.bn, tr.wm, tr.wn, tr.cpr * 16, tr.st, p.tall ? "rows" : "columns(transposed-read)");
+                ns::kNormChunkVecs, p.dtype == NS_DTYPE_BF16 ? "32x32x16_bf16" : "32x32x2_f32", tg.bm, tg.bn, tg.wm,
+                tg.wn, tg.cpr * 16, tg.st, p.tall ? "columns(transposed-read)" : "rows", tp.bm, tp.bn, tp.wm, tp.wn,
+                tp.cpr * 16, tp.st, p.tall ? "X*C" : "C*X", tr.bm, tr.bn, tr.wm, tr.wn, tr.cpr * 16, tr.st,
+                p.tall ? "rows" : "columns(transposed-read)");
   t_cfg = buf;
 }
 

@@ -162,7 +162,7 @@ void replay_frag_reads(const TileCfg& t, int es, bool nat, int rows_region, int 
 void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool coverage, const char* what) {
   const int mode = kind.mode;
   const bool tri = mode_is_tri(mode);
-  const TileCfg t = tile_cfg(dtype, tri, kind.wide_tri);
+  const TileCfg t = tile_cfg(dtype, tri, kind.tri_cls);
   const int es = (int)elem_size(dtype);
   const int EPC = 16 / es, BK = t.cpr * EPC;
   const int NT = t.wm * t.wn * 64, WTM = t.bm / t.wm, WTN = t.bn / t.wn;
@@ -246,7 +246,16 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
             if (jb < k0 || jb >= k0 + BK) continue;
             for (int rg = 0; rg < 4; ++rg) {
               const int j = jb + acc_j(rg, lane), kk = j - k0;
-              if (mode == MODE_UPD_COL && j < g.N) access(g.d_in, (db0 + j) * 4, 16, what);
+              if (mode == MODE_UPD_COL) {
+                // buffer load over the slice's d_bs floats: in range exactly
+                // when j < N (then all 16 bytes are), else it reads zeros
+                const long long off = (long long)(jb * 4) + acc_j(rg, lane) * 4, range = g.d_bs * 4;
+                if ((off < range) != (j < g.N)) fail(std::string(what) + ": d_C buffer range != column range");
+                if (off < range) {
+                  if (off + 16 > range) fail(std::string(what) + ": d_C read straddles the range end");
+                  access(g.d_in, (db0 + j) * 4, 16, what);
+                }
+              }
               for (int a = 0; a < SM; ++a) {
                 const int il = wm * WTM + a * 32 + (lane & 31);
                 if (kk / EPC >= t.cpr) fail(std::string(what) + ": capture chunk outside the stage");

@@ -333,6 +333,8 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
   // registers until the epilogue.
   typedef typename Quad<T>::Raw QRaw;
   const float* din = g.d_in + (size_t)slice * g.d_bs;
+  const __amdgpu_buffer_rsrc_t rD =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(din), (short)0, (int)(g.d_bs * 4), 0x00020000);
 
   // 1 / (||x||_F + eps) from the slice's partial sums of squares (first
   // step only); every wave of every kernel sums them in the same order, so
@@ -395,8 +397,14 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
         for (int rg = 0; rg < 4; ++rg) {
           const int j = jb + acc_j(rg, lane);
           const int kk = j - k0;
+          // d_C[j .. j+3] through a buffer load: a per-lane offset, the
+          // block's column in a scalar and the register group as an
+          // immediate (plain pointer arithmetic here is hoisted out of the
+          // K loop as eight 64-bit addresses); past N it reads zeros
           float4 dj = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-          if (MODE == MODE_UPD_COL && j < g.N) dj = *reinterpret_cast<const float4*>(din + j);
+          if (MODE == MODE_UPD_COL)
+            dj = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rD, (unsigned)(acc_j(rg, lane) * 4), (unsigned)(jb * 4), 0));
 #pragma unroll
           for (int a = 0; a < SM; ++a) {
             const int il = wm * WTM + a * 32 + l32;
@@ -633,29 +641,38 @@ __global__ __launch_bounds__(kNormThreads) void scale_kernel(const NormArgs g) {
 
 // ------------------------------------------------------------- launchers
 
-template <typename T, int MODE, bool WIDE, bool PNAT, bool QNAT>
+template <typename T, int MODE, int CLS, bool PNAT, bool QNAT>
 static hipError_t launch_mode(const GemmArgs& g, hipStream_t st) {
-  constexpr TileCfg t = tile_cfg(std::is_same<T, bf16>::value ? 1 : 0, mode_is_tri(MODE), WIDE);
+  constexpr TileCfg t = tile_cfg(std::is_same<T, bf16>::value ? 1 : 0, mode_is_tri(MODE), CLS);
   const int total = g.tiles_per_slice * g.batch;
   hipLaunchKernelGGL((gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.cpr, t.st, t.occ, MODE, PNAT, QNAT>),
                      dim3(total), dim3(t.wm * t.wn * 64), 0, st, g);
   return hipGetLastError();
 }
 
+template <typename T, int MODE, bool PNAT, bool QNAT>
+static hipError_t launch_tri(int cls, const GemmArgs& g, hipStream_t st) {
+  if (!std::is_same<T, bf16>::value) return launch_mode<T, MODE, TRI_NARROW, PNAT, QNAT>(g, st);
+  switch (cls) {
+    case TRI_WIDE: return launch_mode<T, MODE, TRI_WIDE, PNAT, QNAT>(g, st);
+    case TRI_BIG: return launch_mode<T, MODE, TRI_BIG, PNAT, QNAT>(g, st);
+    default: return launch_mode<T, MODE, TRI_NARROW, PNAT, QNAT>(g, st);
+  }
+}
+
 template <typename T>
 static hipError_t dispatch_mode(const StageKind& k, const GemmArgs& g, hipStream_t st) {
-  const bool wide = k.wide_tri && std::is_same<T, bf16>::value;
   switch (k.mode) {
     case MODE_GRAM:
-      if (k.p_nat) return wide ? launch_mode<T, MODE_GRAM, true, true, true>(g, st)
-                               : launch_mode<T, MODE_GRAM, false, true, true>(g, st);
-      return wide ? launch_mode<T, MODE_GRAM, true, false, false>(g, st)
-                  : launch_mode<T, MODE_GRAM, false, false, false>(g, st);
+      if (k.p_nat) return launch_tri<T, MODE_GRAM, true, true>(k.tri_cls, g, st);
+      return launch_tri<T, MODE_GRAM, false, false>(k.tri_cls, g, st);
     case MODE_POLY:
-      return wide ? launch_mode<T, MODE_POLY, true, false, false>(g, st)
-                  : launch_mode<T, MODE_POLY, false, false, false>(g, st);
-    case MODE_UPD_ROW: return launch_mode<T, MODE_UPD_ROW, false, false, true>(g, st);
-    case MODE_UPD_COL: return launch_mode<T, MODE_UPD_COL, false, false, false>(g, st);
+      // the poly never takes the big tile (see tri_class)
+      return k.tri_cls == TRI_WIDE && std::is_same<T, bf16>::value
+                 ? launch_mode<T, MODE_POLY, TRI_WIDE, false, false>(g, st)
+                 : launch_mode<T, MODE_POLY, TRI_NARROW, false, false>(g, st);
+    case MODE_UPD_ROW: return launch_mode<T, MODE_UPD_ROW, TRI_NARROW, false, true>(g, st);
+    case MODE_UPD_COL: return launch_mode<T, MODE_UPD_COL, TRI_NARROW, false, false>(g, st);
     default: return hipErrorInvalidValue;
   }
 }

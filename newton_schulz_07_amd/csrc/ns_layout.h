@@ -41,6 +41,9 @@ struct TileCfg {
 #ifndef NS_TILE_BF16_TRI_WIDE
 #define NS_TILE_BF16_TRI_WIDE {192, 192, 2, 2, 8, 2, 1}
 #endif
+#ifndef NS_TILE_BF16_TRI_BIG
+#define NS_TILE_BF16_TRI_BIG {256, 256, 2, 4, 8, 2, 1}
+#endif
 #ifndef NS_TILE_BF16_RECT
 #define NS_TILE_BF16_RECT {256, 256, 2, 4, 8, 2, 1}
 #endif
@@ -52,6 +55,7 @@ struct TileCfg {
 #endif
 constexpr TileCfg kTileBf16Tri = NS_TILE_BF16_TRI;
 constexpr TileCfg kTileBf16TriWide = NS_TILE_BF16_TRI_WIDE;
+constexpr TileCfg kTileBf16TriBig = NS_TILE_BF16_TRI_BIG;
 constexpr TileCfg kTileBf16Rect = NS_TILE_BF16_RECT;
 constexpr TileCfg kTileF32Tri = NS_TILE_F32_TRI;
 constexpr TileCfg kTileF32Rect = NS_TILE_F32_RECT;
@@ -64,8 +68,23 @@ constexpr TileCfg kTileF32Rect = NS_TILE_F32_RECT;
 NS_HD constexpr bool use_wide_tri(int dtype, long long batch, long long m) {
   return dtype == 1 && batch * ((m + 127) / 128) * ((m + 127) / 128 + 1) / 2 < 1024;
 }
-NS_HD constexpr TileCfg tile_cfg(int dtype, bool tri, bool wide_tri = false) {
-  return dtype == 1 ? (tri ? (wide_tri ? kTileBf16TriWide : kTileBf16Tri) : kTileBf16Rect)
+// Triangle tile class of a stage: narrow (128), wide (192, see above) or,
+// for the bf16 Gram of a stack with at least four rounds of 256 x 256
+// triangle tiles, big (256): the Gram has a long K (the long side) and a
+// plain epilogue, so the larger tile's halved operand traffic outweighs its
+// diagonal-tile waste.  The poly keeps 128: its epilogue holds the O_A
+// quads of the whole wave tile in registers.
+enum TriClass { TRI_NARROW = 0, TRI_WIDE = 1, TRI_BIG = 2 };
+NS_HD constexpr int tri_class(int dtype, long long batch, long long m, bool gram) {
+  return use_wide_tri(dtype, batch, m) ? TRI_WIDE
+         : (gram && dtype == 1 && batch * ((m + 255) / 256) * ((m + 255) / 256 + 1) / 2 >= 1024) ? TRI_BIG
+                                                                                                 : TRI_NARROW;
+}
+NS_HD constexpr TileCfg tile_cfg(int dtype, bool tri, int tri_cls = TRI_NARROW) {
+  return dtype == 1 ? (tri ? (tri_cls == TRI_WIDE ? kTileBf16TriWide
+                              : tri_cls == TRI_BIG ? kTileBf16TriBig
+                                                   : kTileBf16Tri)
+                           : kTileBf16Rect)
                     : (tri ? kTileF32Tri : kTileF32Rect);
 }
 NS_HD constexpr int elems_per_chunk(int dtype) { return dtype == 1 ? 8 : 4; }

@@ -81,16 +81,16 @@ inline NormArgs norm_args(const Plan& p, const void* x, void* y, float* norms, f
 struct StageKind {
   int mode;
   bool p_nat, q_nat;  // operand read in its natural layout (see ns_layout.h)
-  bool wide_tri;      // 192 x 192 triangle tile
+  int tri_cls;        // triangle tile class (TriClass)
 };
 
-inline bool plan_wide_tri(const Plan& p) { return use_wide_tri(p.dtype, p.batch, p.m); }
+inline int plan_tri_class(const Plan& p, bool gram) { return tri_class(p.dtype, p.batch, p.m, gram); }
 
 // A = X Xᵀ (rows <= cols: rows of X are K-contiguous) or Xᵀ X (rows > cols:
 // columns of X, read in X's natural layout), mirrored into one m x m matrix.
 inline GemmArgs gram_args(const Plan& p, const void* x, void* oa, float* da, StageKind* kind,
                           const float* d_norm = nullptr) {
-  const TileCfg t = tile_cfg(p.dtype, true, plan_wide_tri(p));
+  const TileCfg t = tile_cfg(p.dtype, true, plan_tri_class(p, true));
   GemmArgs g{};
   g.P = g.Q = x;
   g.p_bs = g.q_bs = p.rows * p.cols;
@@ -108,14 +108,14 @@ inline GemmArgs gram_args(const Plan& p, const void* x, void* oa, float* da, Sta
   g.d_norm = d_norm;
   g.norm_n = p.norm_chunks;
   g.eps = kNormEps;
-  *kind = StageKind{MODE_GRAM, p.tall, p.tall, plan_wide_tri(p)};
+  *kind = StageKind{MODE_GRAM, p.tall, p.tall, plan_tri_class(p, true)};
   return g;
 }
 
 // C = a I + b A + c A A from the split A, written split the same way.
 inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* oc, float* dc, float a,
                           float b, float c, StageKind* kind) {
-  const TileCfg t = tile_cfg(p.dtype, true, plan_wide_tri(p));
+  const TileCfg t = tile_cfg(p.dtype, true, plan_tri_class(p, false));
   GemmArgs g{};
   g.P = g.Q = oa;
   g.p_bs = g.q_bs = p.m * p.m;
@@ -136,7 +136,7 @@ inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* 
   g.ca = a;
   g.cb = b;
   g.cc = c;
-  *kind = StageKind{MODE_POLY, false, false, plan_wide_tri(p)};
+  *kind = StageKind{MODE_POLY, false, false, plan_tri_class(p, false)};
   return g;
 }
 
@@ -152,7 +152,7 @@ inline GemmArgs update_args(const Plan& p, const void* x, const void* oc, const 
     g.Q = x;
     g.q_bs = p.rows * p.cols;
     g.ldq = (int)p.cols;
-    *kind = StageKind{MODE_UPD_ROW, false, true, false};
+    *kind = StageKind{MODE_UPD_ROW, false, true, TRI_NARROW};
   } else {  // P = rows of X, Q = rows of O_C (C is symmetric)
     g.P = x;
     g.p_bs = p.rows * p.cols;
@@ -160,7 +160,7 @@ inline GemmArgs update_args(const Plan& p, const void* x, const void* oc, const 
     g.Q = oc;
     g.q_bs = p.m * p.m;
     g.ldq = (int)p.m;
-    *kind = StageKind{MODE_UPD_COL, false, false, false};
+    *kind = StageKind{MODE_UPD_COL, false, false, TRI_NARROW};
   }
   g.M = (int)p.rows;
   g.N = (int)p.cols;

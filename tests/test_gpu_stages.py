@@ -74,6 +74,28 @@ def test_gram(dtype, shape):
         assert np.all(np.abs(d - np.diag(A)) <= K * U * np.diag(S))
 
 
+@pytest.mark.parametrize("shape", [(400, 264, 520), (400, 520, 264)])
+def test_gram_large_stack(shape):
+    # 400 slices with m = 264 give 1200 lower-triangle tiles at 256 x 256:
+    # the bf16 Gram then runs its 256-tile instance (ragged: 264 = 256 + 8)
+    dev = device()
+    x = gaussian(shape, 250 + shape[1], torch.bfloat16, scale=0.05)
+    a_off, a_diag = ns.ns_stage_gram(x.to(dev))
+    torch.cuda.synchronize()
+    assert torch.equal(a_off, a_off.transpose(1, 2)), "Gram must be bitwise symmetric"
+    assert torch.all(a_off.diagonal(dim1=1, dim2=2) == 0)
+    X = to64(x)
+    K = max(shape[1:])
+    for s in (0, 1, 199, 398, 399):
+        A = ns_oracle.gram_matrix(X[s])
+        S = ns_oracle.gram_matrix(np.abs(X[s]))
+        off = to64(a_off[s])
+        mask = ~np.eye(A.shape[0], dtype=bool)
+        tol = store_rel(torch.bfloat16) * np.abs(A) + K * U * S
+        assert np.all(np.abs(off - A)[mask] <= tol[mask]), s
+        assert np.all(np.abs(to64(a_diag[s]) - np.diag(A)) <= K * U * np.diag(S)), s
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("m,batch", [(256, 1), (264, 3), (8, 2), (520, 1), (136, 4)])
 def test_poly(dtype, m, batch):
