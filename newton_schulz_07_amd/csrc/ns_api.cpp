@@ -182,9 +182,10 @@ int launch_stage(int kind_id, const char* what, const Plan& p, const GemmArgs& g
   return check_hip(timed_launch(kind_id, st, [&] { return ns::launch_gemm(p.dtype, k, g, st); }), what);
 }
 
-int run_gram(const void* x, void* oa, float* da, const Plan& p, hipStream_t st, const float* d_norm = nullptr) {
+int run_gram(const void* x, void* oa, float* da, const Plan& p, hipStream_t st, const float* d_norm = nullptr,
+             bool mirror = true) {
   ns::StageKind k;
-  const GemmArgs g = ns::gram_args(p, x, oa, da, &k, d_norm);
+  const GemmArgs g = ns::gram_args(p, x, oa, da, &k, d_norm, mirror);
   return launch_stage(NS_KIND_GRAM, "gram launch", p, g, k, st);
 }
 
@@ -276,7 +277,8 @@ int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows, int
     if (int s = check_hip(hipMemcpyAsync(xtmp, in, bytes, hipMemcpyDeviceToDevice, st), "input copy")) return s;
   for (int s = 1; s <= ns_steps; ++s) {
     const float* dn = (fold && s == 1) ? part : nullptr;  // partial sums of squares -> ||x||_F
-    if (int e = run_gram(buf(s - 1), oa, da, p, st, dn)) return e;
+    // the poly reads A as its lower block triangle when it can (no mirror)
+    if (int e = run_gram(buf(s - 1), oa, da, p, st, dn, !ns::gram_lower_only(p))) return e;
     if (int e = run_poly(oa, da, oc, dc, p, a, b, c, st)) return e;
     if (int e = run_update(buf(s - 1), oc, dc, wbuf(s), p, st, dn)) return e;
   }

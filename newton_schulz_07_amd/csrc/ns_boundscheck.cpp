@@ -7,9 +7,14 @@
 //   * every workgroup id maps to a distinct tile of a valid slice,
 //   * every global load and store stays inside the buffer its pointer names,
 //   * every LDS index stays inside the operand's LDS region,
-//   * every output element (and diagonal entry) is written exactly once.
-// K stages other than the first and the last only move the k offset between
-// those two, so only those two are replayed.
+//   * every output element (and diagonal entry) is written exactly once
+//     (a Gram without its mirror: exactly its lower block triangle),
+//   * in shapes small enough for coverage maps, every load of a matrix some
+//     earlier kernel of the call produced reads only elements it wrote.
+// K stages of one layout other than the first and the last only move the k
+// offset between those two, so only those (and the stages where an operand
+// changes layout) are replayed, except for operands read as their lower
+// block triangle in coverage runs, where every stage is.
 //
 // Build: g++ -O2 -std=c++17 -I<csrc> ns_boundscheck.cpp -o ns_boundscheck
 // Run:   ns_boundscheck dtype batch rows cols steps [dtype batch rows cols steps ...]
@@ -33,6 +38,9 @@ struct Buf {
   size_t bytes;
 };
 std::map<uintptr_t, Buf> g_bufs;
+// elements each buffer's producer wrote (coverage runs): consumers may read
+// only these (or zero-fill past the buffer's range)
+std::map<uintptr_t, std::vector<uint8_t>> g_written;
 long long g_checks = 0;
 int g_fail = 0;
 
@@ -107,7 +115,16 @@ void replay_dma(int wave, int niw, const TileCfg& t, int es, bool pnat, bool qna
       if ((long long)off != want) fail(std::string(what) + ": DMA offset differs from the element's");
       if (want + 16 > range || want >= (long long)kOut)
         fail(std::string(what) + ": in-range load past the slice");
-      access(d.is_p ? g.P : g.Q, (long long)slice * (d.is_p ? g.p_bs : g.q_bs) * es + want, 16, what);
+      const void* src = d.is_p ? g.P : g.Q;
+      const long long ebase = (long long)slice * (d.is_p ? g.p_bs : g.q_bs) + want / es;
+      access(src, ebase * es, 16, what);
+      auto wr = g_written.find(reinterpret_cast<uintptr_t>(src));
+      if (wr != g_written.end())
+        for (int e = 0; e < EPC; ++e)
+          if (wr->second[ebase + e] != 1) {
+            fail(std::string(what) + ": load of an element its producer did not write");
+            break;
+          }
     }
   }
 }
@@ -191,6 +208,8 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
     const int wm = wave / t.wn, wn = wave % t.wn;
     replay_frag_reads(t, es, kind.p_nat, t.bm, WTM, SM, wm * WTM, what);
     replay_frag_reads(t, es, kind.q_nat, t.bn, WTN, SN, wn * WTN, what);
+    if (kind.p_sym) replay_frag_reads(t, es, true, t.bm, WTM, SM, wm * WTM, what);
+    if (kind.q_sym) replay_frag_reads(t, es, true, t.bn, WTN, SN, wn * WTN, what);
   }
 
   for (int w = 0; w < G; ++w) {
@@ -209,12 +228,29 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
       continue;
     }
     const int i0 = ti * t.bm, j0 = tj * t.bn;
-    const int kstages[2] = {0, nk - 1};
-    for (int si = 0; si < (nk > 1 ? 2 : 1); ++si) {
-      const int kt = kstages[si];
-      for (int wave = 0; wave < NW; ++wave)
-        replay_dma(wave, NIW, t, es, kind.p_nat, kind.q_nat, kt * BK, g, slice, i0, j0, STAGE, kt % t.st, LDS, what);
+    // first stage of natural-layout reads of each operand (mirrors gemm_kernel)
+    const int nat_p = kind.p_sym ? sym_nat_from(i0, g.sym_tile, BK) : (kind.p_nat ? 0 : 0x7fffffff);
+    const int nat_q = kind.q_sym ? sym_nat_from(j0, g.sym_tile, BK) : (kind.q_nat ? 0 : 0x7fffffff);
+    if (kind.p_sym || kind.q_sym) {
+      if (!sym_layout_ok(std::max(kind.p_sym ? t.bm : 0, kind.q_sym ? t.bn : 0), g.sym_tile, BK, t.st))
+        fail(std::string(what) + ": symmetric operand layout not valid for this tile");
+      if ((kind.p_sym && nat_p < nk && nat_p % t.st) || (kind.q_sym && nat_q < nk && nat_q % t.st))
+        fail(std::string(what) + ": layout phase does not start at a multiple of the ring depth");
+      if (kind.p_sym && kind.q_sym && nat_q > nat_p) fail(std::string(what) + ": Q must switch layouts first");
     }
+    std::vector<int> kst;
+    if (coverage && (kind.p_sym || kind.q_sym)) {
+      for (int kt = 0; kt < nk; ++kt) kst.push_back(kt);
+    } else {
+      kst.push_back(0);
+      if (nk > 1) kst.push_back(nk - 1);
+      for (int b : {nat_p - 1, nat_p, nat_q - 1, nat_q})
+        if (b > 0 && b < nk - 1) kst.push_back(b);
+    }
+    for (int kt : kst)
+      for (int wave = 0; wave < NW; ++wave)
+        replay_dma(wave, NIW, t, es, kt >= nat_p, kt >= nat_q, kt * BK, g, slice, i0, j0, STAGE, kt % t.st, LDS,
+                   what);
     // norm folded into the first step: the slice's partial sums of squares
     if (mode != MODE_POLY && g.d_norm != nullptr)
       for (int i = 0; i < g.norm_n; ++i) access(g.d_norm, ((long long)slice * g.norm_n + i) * 4, 4, what);
@@ -224,6 +260,16 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
     const int RCQ = t.bn / EPC;
     for (int kt = 0; kt < nk && mode != MODE_GRAM; ++kt) {
       const int k0 = kt * BK, slot = kt % t.st;
+      if (mode == MODE_POLY && kt >= nat_p) {
+        bool any = false;
+        for (int wn = 0; wn < t.wn; ++wn)
+          for (int b = 0; b < SN; ++b) {
+            const int jb = j0 + wn * WTN + b * 32;
+            any = any || (jb >= k0 && jb < k0 + BK);
+          }
+        if (any) fail(std::string(what) + ": poly capture at a stage where P is not K-contiguous");
+        continue;  // the kernel compiles no capture in its natural-layout phase
+      }
       for (int tid = 0; tid < NT; ++tid) {
         const int lane = tid & 63, wave = tid >> 6, wm = wave / t.wn, wn = wave % t.wn;
         if (mode == MODE_UPD_ROW) {
@@ -331,16 +377,21 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
   }
   if (coverage) {
     long long bad = 0;
+    // a triangle kernel without a transposed store writes its lower block
+    // triangle only (tiles of t.bm rows; diagonal tiles whole)
+    const bool lower_only = tri && g.out_t == nullptr;
     for (int s = 0; s < g.batch; ++s)
       for (int i = 0; i < g.M; ++i)
         for (int j = 0; j < g.N; ++j) {
           const uint8_t c = cover[(long long)s * g.o_bs + (long long)i * g.ldo + j];
-          if (c != 1) ++bad;
+          const uint8_t want = (lower_only && j / t.bm > i / t.bm) ? 0 : 1;
+          if (c != want) ++bad;
           if (!tcover.empty() && tcover[(long long)s * g.ot_bs + (long long)j * g.ldt + i] != 1) ++bad;
         }
     for (size_t i = 0; i < dcover.size(); ++i)
       if (dcover[i] != 1) ++bad;
     if (bad) fail(std::string(what) + ": " + std::to_string(bad) + " output elements not written exactly once");
+    g_written[reinterpret_cast<uintptr_t>(g.out)] = cover;
   }
 }
 
@@ -372,6 +423,7 @@ void replay_norm(const NormArgs& g, int batch, bool scale, const char* what) {
 // Replays one ns_orthogonalize call as the driver sequences it.
 void replay_call(int dtype, long long batch, long long rows, long long cols, int steps, bool alias) {
   g_bufs.clear();
+  g_written.clear();
   const Plan p = make_plan(batch, rows, cols, dtype);
   const int es = (int)elem_size(dtype);
   const size_t xbytes = (size_t)batch * rows * cols * es;
@@ -401,7 +453,7 @@ void replay_call(int dtype, long long batch, long long rows, long long cols, int
     if (s != 1 && s != steps && s != 2) continue;  // later steps differ only in which buffer is which
     const float* dn = (fold && s == 1) ? part : nullptr;
     StageKind kind;
-    GemmArgs g = gram_args(p, buf(s - 1), oa, da, &kind, dn);
+    GemmArgs g = gram_args(p, buf(s - 1), oa, da, &kind, dn, !gram_lower_only(p));
     replay_gemm(g, kind, dtype, cov, "gram");
     g = poly_args(p, oa, da, oc, dc, 3.4445f, -4.775f, 2.0315f, &kind);
     replay_gemm(g, kind, dtype, cov, "poly");

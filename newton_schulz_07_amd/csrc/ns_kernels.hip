@@ -173,8 +173,15 @@ __device__ __forceinline__ int nat_lane_byte(int rb, int h, int lane, int rc, fl
   return nat_lane_byte_f32(rb, h, lane, rc);
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int CPR, int ST, int OCC, int MODE, bool PNAT, bool QNAT>
-__global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g) {
+// OCC workgroups of WM x WN waves per CU: at least OCC WM WN / 4 waves on each
+// of the CU's four SIMDs (HIP's second launch bound), which caps the VGPRs.
+template <typename T, int BM, int BN, int WM, int WN, int CPR, int ST, int OCC, int MODE, int PL, int QL>
+__global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_kernel(const GemmArgs g) {
+  // operand layouts (OperandLayout): which read paths each operand needs
+  constexpr bool PNAT = PL == LAY_NAT, QNAT = QL == LAY_NAT;
+  constexpr bool P_KC = PL != LAY_NAT, P_NT = PL != LAY_KCONT;  // K-contiguous / natural reads of P
+  constexpr bool Q_KC = QL != LAY_NAT, Q_NT = QL != LAY_KCONT;
+  constexpr bool HAS_SYM = PL == LAY_SYM || QL == LAY_SYM;
   constexpr int NT = WM * WN * 64, NW = WM * WN;
   constexpr int EPC = Elem<T>::kChunk;
   constexpr int ES = (int)sizeof(T);
@@ -205,6 +212,9 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
   if (mode_is_tri(MODE)) tri_decode(q, ti, tj);
   else rect_decode(q, g.tiles_m, g.tiles_n, ti, tj);
   const int i0 = ti * BM, j0 = tj * BN;
+  // first stage an operand reads in its natural layout (never: a large value)
+  const int nat_from_p = PL == LAY_SYM ? sym_nat_from(i0, g.sym_tile, BK) : (PNAT ? 0 : 0x7fffffff);
+  const int nat_from_q = QL == LAY_SYM ? sym_nat_from(j0, g.sym_tile, BK) : (QNAT ? 0 : 0x7fffffff);
 
   // Buffer descriptors over the two operand slices: an offset at or past the
   // slice end reads as zero, which fills rows past M / N and k past K.
@@ -215,44 +225,55 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
   constexpr unsigned kOutOfRange = 0x80000000u;
 
   // Per-lane source of each of this wave's load instructions: the byte
-  // offset at k0 = 0 (past the slice end for rows past M / N).  From one
-  // stage to the next an operand's offsets move by a wave-uniform step.
-  unsigned src_off[NIW];
-#pragma unroll
-  for (int t = 0; t < NIW; ++t) {
-    const DmaSrc d = dma_src(wave * NIW + t, lane, BM, BN, CPR, EPC, PNAT, QNAT, ES);
-    const bool nat = d.is_p ? PNAT : QNAT;
+  // offset at k0 = 0 (past the slice end for rows past M / N), K-contiguous
+  // or natural per the operand's layout, plus the natural-layout offset of a
+  // LAY_SYM operand.  From one stage to the next an operand's offsets move by
+  // a wave-uniform step.
+  unsigned src_off[NIW], src_alt[HAS_SYM ? NIW : 1];
+  auto src_of = [&](const DmaSrc& d, bool nat) __attribute__((always_inline)) -> unsigned {
     const int ld = d.is_p ? g.ldp : g.ldq;
     const int g_row = (d.is_p ? i0 : j0) + d.row;  // tile row (KCONT) or column (NAT)
     const bool ok = g_row < (d.is_p ? g.M : g.N);
     const size_t off = nat ? ((size_t)d.kpos * ld + g_row) * ES : ((size_t)g_row * ld + d.kpos) * ES;
-    src_off[t] = ok ? (unsigned)off : kOutOfRange;
+    return ok ? (unsigned)off : kOutOfRange;
+  };
+#pragma unroll
+  for (int t = 0; t < NIW; ++t) {
+    const int idx = wave * NIW + t;
+    src_off[t] = src_of(dma_src(idx, lane, BM, BN, CPR, EPC, PNAT, QNAT, ES), idx * 64 < LP ? PNAT : QNAT);
+    if constexpr (HAS_SYM) src_alt[t] = src_of(dma_src(idx, lane, BM, BN, CPR, EPC, true, true, ES), true);
   }
-  const unsigned step_p = PNAT ? (unsigned)(BK * g.ldp * ES) : (unsigned)(BK * ES);
-  const unsigned step_q = QNAT ? (unsigned)(BK * g.ldq * ES) : (unsigned)(BK * ES);
+  const unsigned step_kc = (unsigned)(BK * ES);
+  const unsigned step_np = (unsigned)(BK * g.ldp * ES), step_nq = (unsigned)(BK * g.ldq * ES);
   // Loads of stage kt into ring slot `slot`.  When the whole stage lies
   // inside K (always, for K a multiple of BK) only rows past M / N need the
   // zero fill, and their offset already starts past the slice end; otherwise
   // each lane also checks its own k position.
-  auto issue = [&](int kt, int slot) {
+  auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
     const int k0 = kt * BK;
+    // natural-layout reads this stage (compile-time unless LAY_SYM)
+    const bool pn = PL == LAY_SYM ? kt >= nat_from_p : PNAT;
+    const bool qn = QL == LAY_SYM ? kt >= nat_from_q : QNAT;
+    auto off_of = [&](int t, bool is_p) __attribute__((always_inline)) -> unsigned {
+      const bool nat = is_p ? pn : qn;
+      const bool alt = HAS_SYM && (is_p ? PL == LAY_SYM : QL == LAY_SYM) && nat;
+      return (alt ? src_alt[HAS_SYM ? t : 0] : src_off[t]) + (unsigned)kt * (nat ? (is_p ? step_np : step_nq) : step_kc);
+    };
     if (k0 + BK <= g.K) {
 #pragma unroll
       for (int t = 0; t < NIW; ++t) {
         const int idx = wave * NIW + t;  // wave-uniform
         const bool is_p = idx * 64 < LP;
-        dma16(lds_addr(lds + slot * STAGE + idx * 64), src_off[t] + (unsigned)kt * (is_p ? step_p : step_q),
-              is_p ? rP : rQ);
+        dma16(lds_addr(lds + slot * STAGE + idx * 64), off_of(t, is_p), is_p ? rP : rQ);
       }
     } else {
 #pragma unroll
       for (int t = 0; t < NIW; ++t) {
         const int idx = wave * NIW + t;
         const bool is_p = idx * 64 < LP;
-        const int kpos = dma_src(idx, lane, BM, BN, CPR, EPC, PNAT, QNAT, ES).kpos;
-        const unsigned off =
-            (k0 + kpos < g.K) ? src_off[t] + (unsigned)kt * (is_p ? step_p : step_q) : kOutOfRange;
-        dma16(lds_addr(lds + slot * STAGE + idx * 64), off, is_p ? rP : rQ);
+        const int kpos = dma_src(idx, lane, BM, BN, CPR, EPC, pn, qn, ES).kpos;
+        dma16(lds_addr(lds + slot * STAGE + idx * 64), (k0 + kpos < g.K) ? off_of(t, is_p) : kOutOfRange,
+              is_p ? rP : rQ);
       }
     }
   };
@@ -274,47 +295,52 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
   constexpr int QOFF = LP * 16;                    // Q region within a stage
   constexpr int NSP = nat_step_bytes(RCP, ES), NSQ = nat_step_bytes(RCQ, ES);
   static_assert(CPR == 4 || CPR == 8, "fragment addressing assumes 4 or 8 chunks per row");
-  int kcp[PNAT ? 1 : KS], kcq[QNAT ? 1 : KS];
-  int natp[PNAT ? SM : 1][NH], natq[QNAT ? SN : 1][NH];
-  if constexpr (!PNAT) {
+  int kcp[P_KC ? KS : 1], kcq[Q_KC ? KS : 1];
+  int natp[P_NT ? SM : 1][NH], natq[Q_NT ? SN : 1][NH];
+  if constexpr (P_KC) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) kcp[s] = kc_lane_byte(wm * WTM, s, lane, CPR);
-  } else {
+  }
+  if constexpr (P_NT) {
 #pragma unroll
     for (int a = 0; a < SM; ++a)
 #pragma unroll
       for (int h = 0; h < NH; ++h) natp[a][h] = nat_lane_byte(wm * WTM + 32 * a, h, lane, RCP, T());
   }
-  if constexpr (!QNAT) {
+  if constexpr (Q_KC) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) kcq[s] = kc_lane_byte(wn * WTN, s, lane, CPR) + QOFF;
-  } else {
+  }
+  if constexpr (Q_NT) {
 #pragma unroll
     for (int b = 0; b < SN; ++b)
 #pragma unroll
       for (int h = 0; h < NH; ++h) natq[b][h] = nat_lane_byte(wn * WTN + 32 * b, h, lane, RCQ, T()) + QOFF;
   }
   const char* lb = reinterpret_cast<const char*>(lds);
-  auto load_step = [&](int slot, int s, uint4 (&pf)[SM], uint4 (&qf)[SN]) {
+  // fragments of step s; pn / qn (std::integral_constant) select the natural
+  // layout reads for this stage
+  auto load_step = [&](int slot, int s, auto pn, auto qn, uint4 (&pf)[SM], uint4 (&qf)[SN])
+                       __attribute__((always_inline)) {
     const char* st = lb + slot * STAGE * 16;
 #pragma unroll
     for (int a = 0; a < SM; ++a) {
-      if constexpr (PNAT) pf[a] = nat_frag(st + s * NSP, natp[a], T());
-      else pf[a] = *reinterpret_cast<const uint4*>(st + kcp[s ^ kc_sigma(a, CPR)] + a * 32 * CPR * 16);
+      if constexpr (decltype(pn)::value) pf[a] = nat_frag(st + s * NSP, natp[P_NT ? a : 0], T());
+      else pf[a] = *reinterpret_cast<const uint4*>(st + kcp[P_KC ? (s ^ kc_sigma(a, CPR)) : 0] + a * 32 * CPR * 16);
     }
 #pragma unroll
     for (int b = 0; b < SN; ++b) {
-      if constexpr (QNAT) qf[b] = nat_frag(st + s * NSQ, natq[b], T());
-      else qf[b] = *reinterpret_cast<const uint4*>(st + kcq[s ^ kc_sigma(b, CPR)] + b * 32 * CPR * 16);
+      if constexpr (decltype(qn)::value) qf[b] = nat_frag(st + s * NSQ, natq[Q_NT ? b : 0], T());
+      else qf[b] = *reinterpret_cast<const uint4*>(st + kcq[Q_KC ? (s ^ kc_sigma(b, CPR)) : 0] + b * 32 * CPR * 16);
     }
   };
   // fragments of step s + 1 are read while the MFMAs of step s run
-  auto compute = [&](int slot) {
+  auto compute = [&](int slot, auto pn, auto qn) __attribute__((always_inline)) {
     uint4 pf[2][SM], qf[2][SN];
-    load_step(slot, 0, pf[0], qf[0]);
+    load_step(slot, 0, pn, qn, pf[0], qf[0]);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if (s + 1 < KS) load_step(slot, s + 1, pf[(s + 1) & 1], qf[(s + 1) & 1]);
+      if (s + 1 < KS) load_step(slot, s + 1, pn, qn, pf[(s + 1) & 1], qf[(s + 1) & 1]);
       // keep the scheduler from sinking these reads back to their uses
       if (NS_FRAG_BARRIER) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -323,6 +349,8 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
         for (int b = 0; b < SN; ++b) mfma_chunk(acc[a][b], qf[s & 1][b], pf[s & 1][a], T());
     }
   };
+  typedef std::integral_constant<bool, true> Nat;
+  typedef std::integral_constant<bool, false> Kc;
 
   // Epilogue operands captured while they pass through LDS.  The update's
   // diagonal term d_C ⊙ X needs X at the output position, which is the
@@ -366,7 +394,7 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) obuf[a][b][rg] = QRaw{};
   }
-  auto capture = [&](int slot, int kt) {
+  auto capture = [&](int slot, int kt) __attribute__((always_inline)) {
     const int k0 = kt * BK;
     const uint4* Ps = lds + slot * STAGE;
     const uint4* Qs = Ps + LP;
@@ -433,8 +461,10 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
   // (kt-1) % ST is no longer read, so stage kt+ST-1 can be loaded into it.
   // The loop runs in groups of ST stages (then a tail of fewer) so that every
   // slot index, and with it every LDS address, is a compile-time constant.
+  // With LAY_SYM operands it runs in up to three phases of fixed layouts,
+  // each starting at a multiple of ST (sym_tile / BK is a multiple of ST).
   const int nk = (g.K + BK - 1) / BK;
-  auto stage = [&](int kt, int u) {  // u == kt % ST
+  auto stage = [&](int kt, int u, auto pn, auto qn) __attribute__((always_inline)) {  // u == kt % ST
     const int after = nk - 1 - kt;   // stages issued after kt, capped at ST-2
     if (after >= ST - 2) wait_vm_lgkm0<NIW * (ST - 2)>();
     else if (ST > 3 && after == 2) wait_vm_lgkm0<NIW * 2>();
@@ -442,20 +472,43 @@ __global__ __launch_bounds__(WM* WN * 64, OCC) void gemm_kernel(const GemmArgs g
     else wait_vm_lgkm0<0>();
     ring_barrier();
     if (kt + ST - 1 < nk) issue(kt + ST - 1, (u + ST - 1) % ST);
-    compute(u);
-    if (MODE != MODE_GRAM) capture(u, kt);
+    compute(u, pn, qn);
+    // the poly's O_A capture happens at the stage covering the tile's own
+    // columns, left of its diagonal, where P is K-contiguous
+    if constexpr (MODE != MODE_GRAM && !(MODE == MODE_POLY && decltype(pn)::value)) capture(u, kt);
+  };
+  auto phase = [&](int kt_begin, int kt_end, auto pn, auto qn) __attribute__((always_inline)) {  // kt_begin % ST == 0
+    int kt0 = kt_begin;
+    for (; kt0 + ST <= kt_end; kt0 += ST) {
+#pragma unroll
+      for (int u = 0; u < ST; ++u) stage(kt0 + u, u, pn, qn);
+    }
+#pragma unroll
+    for (int u = 0; u < ST - 1; ++u)
+      if (kt0 + u < kt_end) stage(kt0 + u, u, pn, qn);
   };
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s)
     if (s < nk) issue(s, s);
-  int kt0 = 0;
-  for (; kt0 + ST <= nk; kt0 += ST) {
-#pragma unroll
-    for (int u = 0; u < ST; ++u) stage(kt0 + u, u);
+  if constexpr (PL == LAY_SYM && QL == LAY_SYM) {
+    // both operands symmetric: a lower-triangle tile (j0 <= i0) switches Q
+    // to natural-layout reads first
+    static_assert(mode_is_tri(MODE), "two symmetric operands need j0 <= i0");
+    const int np = nat_from_p < nk ? nat_from_p : nk, nq = nat_from_q < nk ? nat_from_q : nk;
+    phase(0, nq, Kc(), Kc());
+    phase(nq, np, Kc(), Nat());
+    phase(np, nk, Nat(), Nat());
+  } else if constexpr (PL == LAY_SYM) {
+    const int np = nat_from_p < nk ? nat_from_p : nk;
+    phase(0, np, Kc(), std::integral_constant<bool, QNAT>());
+    phase(np, nk, Nat(), std::integral_constant<bool, QNAT>());
+  } else if constexpr (QL == LAY_SYM) {
+    const int nq = nat_from_q < nk ? nat_from_q : nk;
+    phase(0, nq, std::integral_constant<bool, PNAT>(), Kc());
+    phase(nq, nk, std::integral_constant<bool, PNAT>(), Nat());
+  } else {
+    phase(0, nk, std::integral_constant<bool, PNAT>(), std::integral_constant<bool, QNAT>());
   }
-#pragma unroll
-  for (int u = 0; u < ST - 1; ++u)
-    if (kt0 + u < nk) stage(kt0 + u, u);
   wait_vm_lgkm0<0>();
   __syncthreads();
 
@@ -641,38 +694,46 @@ __global__ __launch_bounds__(kNormThreads) void scale_kernel(const NormArgs g) {
 
 // ------------------------------------------------------------- launchers
 
-template <typename T, int MODE, int CLS, bool PNAT, bool QNAT>
+template <typename T, int MODE, int CLS, int PL, int QL>
 static hipError_t launch_mode(const GemmArgs& g, hipStream_t st) {
   constexpr TileCfg t = tile_cfg(std::is_same<T, bf16>::value ? 1 : 0, mode_is_tri(MODE), CLS);
   const int total = g.tiles_per_slice * g.batch;
-  hipLaunchKernelGGL((gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.cpr, t.st, t.occ, MODE, PNAT, QNAT>),
+  hipLaunchKernelGGL((gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.cpr, t.st, t.occ, MODE, PL, QL>),
                      dim3(total), dim3(t.wm * t.wn * 64), 0, st, g);
   return hipGetLastError();
 }
 
-template <typename T, int MODE, bool PNAT, bool QNAT>
+template <typename T, int MODE, int PL, int QL>
 static hipError_t launch_tri(int cls, const GemmArgs& g, hipStream_t st) {
-  if (!std::is_same<T, bf16>::value) return launch_mode<T, MODE, TRI_NARROW, PNAT, QNAT>(g, st);
+  if (!std::is_same<T, bf16>::value) return launch_mode<T, MODE, TRI_NARROW, PL, QL>(g, st);
   switch (cls) {
-    case TRI_WIDE: return launch_mode<T, MODE, TRI_WIDE, PNAT, QNAT>(g, st);
-    case TRI_BIG: return launch_mode<T, MODE, TRI_BIG, PNAT, QNAT>(g, st);
-    default: return launch_mode<T, MODE, TRI_NARROW, PNAT, QNAT>(g, st);
+    case TRI_WIDE: return launch_mode<T, MODE, TRI_WIDE, PL, QL>(g, st);
+    case TRI_BIG: return launch_mode<T, MODE, TRI_BIG, PL, QL>(g, st);
+    default: return launch_mode<T, MODE, TRI_NARROW, PL, QL>(g, st);
   }
 }
 
 template <typename T>
 static hipError_t dispatch_mode(const StageKind& k, const GemmArgs& g, hipStream_t st) {
+  const bool wide = k.tri_cls == TRI_WIDE && std::is_same<T, bf16>::value;
   switch (k.mode) {
     case MODE_GRAM:
-      if (k.p_nat) return launch_tri<T, MODE_GRAM, true, true>(k.tri_cls, g, st);
-      return launch_tri<T, MODE_GRAM, false, false>(k.tri_cls, g, st);
+      if (k.p_nat) return launch_tri<T, MODE_GRAM, LAY_NAT, LAY_NAT>(k.tri_cls, g, st);
+      return launch_tri<T, MODE_GRAM, LAY_KCONT, LAY_KCONT>(k.tri_cls, g, st);
     case MODE_POLY:
       // the poly never takes the big tile (see tri_class)
-      return k.tri_cls == TRI_WIDE && std::is_same<T, bf16>::value
-                 ? launch_mode<T, MODE_POLY, TRI_WIDE, false, false>(g, st)
-                 : launch_mode<T, MODE_POLY, TRI_NARROW, false, false>(g, st);
-    case MODE_UPD_ROW: return launch_mode<T, MODE_UPD_ROW, TRI_NARROW, false, true>(g, st);
-    case MODE_UPD_COL: return launch_mode<T, MODE_UPD_COL, TRI_NARROW, false, false>(g, st);
+      // lower-triangle reads of A: bf16, 128 tile (see gram_lower_only)
+      if (k.p_sym && k.q_sym && std::is_same<T, bf16>::value && !wide)
+        return launch_mode<bf16, MODE_POLY, TRI_NARROW, LAY_SYM, LAY_SYM>(g, st);
+      if (k.p_sym || k.q_sym) return hipErrorInvalidValue;
+      return wide ? launch_mode<T, MODE_POLY, TRI_WIDE, LAY_KCONT, LAY_KCONT>(g, st)
+                  : launch_mode<T, MODE_POLY, TRI_NARROW, LAY_KCONT, LAY_KCONT>(g, st);
+    case MODE_UPD_ROW:
+      if (k.p_sym || k.q_sym) return hipErrorInvalidValue;
+      return launch_mode<T, MODE_UPD_ROW, TRI_NARROW, LAY_KCONT, LAY_NAT>(g, st);
+    case MODE_UPD_COL:
+      if (k.p_sym || k.q_sym) return hipErrorInvalidValue;
+      return launch_mode<T, MODE_UPD_COL, TRI_NARROW, LAY_KCONT, LAY_KCONT>(g, st);
     default: return hipErrorInvalidValue;
   }
 }

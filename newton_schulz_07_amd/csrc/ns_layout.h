@@ -217,6 +217,23 @@ NS_HD int nat_lane_byte_f32(int rb, int e, int lane, int rc) {
 }
 NS_HD constexpr int nat_step_bytes(int rc, int esize) { return (esize == 2 ? 16 : 8) * rc * 16; }
 
+// Operand layouts: K-contiguous rows (KCONT), the stored matrix read down its
+// columns (NAT), or a symmetric matrix of which only the lower block triangle
+// is stored (SYM: tiles of sym_tile rows, diagonal tiles whole).  A SYM
+// operand reads rows r0 .. r0 + R of k block [k0, k0 + BK) as K-contiguous
+// rows while that k block lies at or left of r0's diagonal block, and from
+// the transposed, stored tile (a NAT read) once it lies to the right: with
+// sym_tile a multiple of BK and R <= sym_tile, every stage then reads stored
+// elements only (the row block spans at most two stored blocks, and the
+// right-hand k blocks are at or below the diagonal of both).  The kernel
+// runs the K loop in phases of fixed layouts that start at multiples of the
+// ring depth st, so sym_tile / BK must also be a multiple of st.
+enum OperandLayout { LAY_KCONT = 0, LAY_NAT = 1, LAY_SYM = 2 };
+NS_HD constexpr int sym_nat_from(int r0, int sym_tile, int bk) { return (r0 / sym_tile + 1) * sym_tile / bk; }
+NS_HD constexpr bool sym_layout_ok(int rows, int sym_tile, int bk, int st) {
+  return sym_tile > 0 && sym_tile % bk == 0 && (sym_tile / bk) % st == 0 && rows <= sym_tile;
+}
+
 // MFMA operand roles: the A operand is the Q tile (output column j), the B
 // operand the P tile (output row i).  Register r of lane l of a 32x32 block
 // then holds row i = l % 32 and column j = 8 (r / 4) + 4 (l / 32) + r % 4,
@@ -258,6 +275,7 @@ struct GemmArgs {
   const float* d_norm;
   int norm_n;
   float eps;
+  int sym_tile;       // stored tile of LAY_SYM operands (rows of the producer's tiles)
 };
 
 // Normalisation: per-slice sum of squares over 32 KiB blocks, then a scale

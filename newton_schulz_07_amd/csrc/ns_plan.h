@@ -82,14 +82,28 @@ struct StageKind {
   int mode;
   bool p_nat, q_nat;  // operand read in its natural layout (see ns_layout.h)
   int tri_cls;        // triangle tile class (TriClass)
+  bool p_sym = false, q_sym = false;  // LAY_SYM operand (lower block triangle stored)
 };
 
 inline int plan_tri_class(const Plan& p, bool gram) { return tri_class(p.dtype, p.batch, p.m, gram); }
 
 // A = X Xᵀ (rows <= cols: rows of X are K-contiguous) or Xᵀ X (rows > cols:
 // columns of X, read in X's natural layout), mirrored into one m x m matrix.
+// The poly can read A as its lower block triangle (LAY_SYM) when the Gram's
+// tile is a multiple of the poly's K stage and at least as tall as the
+// poly's tile; the Gram then stores no mirror.
+// (The kernels instantiate that read for the bf16 poly's 128 tile.)
+inline bool gram_lower_only(const Plan& p) {
+  const TileCfg tg = tile_cfg(p.dtype, true, plan_tri_class(p, true));
+  const TileCfg tp = tile_cfg(p.dtype, true, plan_tri_class(p, false));
+  return p.dtype == 1 && plan_tri_class(p, false) == TRI_NARROW &&
+         sym_layout_ok(tp.bm, tg.bm, tp.cpr * (16 / (int)elem_size(p.dtype)), tp.st);
+}
+
+// mirror: also store the transposes of the off-diagonal tiles (a whole
+// symmetric A); otherwise only the lower block triangle is stored.
 inline GemmArgs gram_args(const Plan& p, const void* x, void* oa, float* da, StageKind* kind,
-                          const float* d_norm = nullptr) {
+                          const float* d_norm = nullptr, bool mirror = true) {
   const TileCfg t = tile_cfg(p.dtype, true, plan_tri_class(p, true));
   GemmArgs g{};
   g.P = g.Q = x;
@@ -100,7 +114,8 @@ inline GemmArgs gram_args(const Plan& p, const void* x, void* oa, float* da, Sta
   g.tiles_m = g.tiles_n = tiles_of(p.m, t.bm);
   g.tiles_per_slice = g.tiles_m * (g.tiles_m + 1) / 2;
   g.batch = (int)p.batch;
-  g.out = g.out_t = oa;
+  g.out = oa;
+  g.out_t = mirror ? oa : nullptr;
   g.o_bs = g.ot_bs = p.m * p.m;
   g.ldo = g.ldt = (int)p.m;
   g.d_out = da;
@@ -137,6 +152,10 @@ inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* 
   g.cb = b;
   g.cc = c;
   *kind = StageKind{MODE_POLY, false, false, plan_tri_class(p, false)};
+  if (gram_lower_only(p)) {  // read A as its lower block triangle
+    kind->p_sym = kind->q_sym = true;
+    g.sym_tile = tile_cfg(p.dtype, true, plan_tri_class(p, true)).bm;
+  }
   return g;
 }
 
