@@ -358,19 +358,56 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
       if (coverage)
         for (int e = 0; e < EPC; ++e) cover[ob + (long long)i * g.ldo + j + e]++;
     }
-    // step 3: transposed store
+    // step 3: transposed store (bf16: transposing LDS reads, mirror_lane)
     if (g.out_t != nullptr && !diag_tile) {
       const long long tb = (long long)slice * g.ot_bs;
-      const int RCH = t.bm / EPC;
-      for (int qd = 0; qd < t.bn * RCH; ++qd) {
-        const int jl = qd % t.bn, rc = qd / t.bn, j = j0 + jl, i = i0 + rc * EPC;
-        if (j >= g.N || i >= g.M) continue;
-        if (((long long)(rc * EPC + EPC - 1) * SROW + jl) * es + es > (long long)LDS * 16)
-          fail(std::string(what) + ": transposed read outside LDS");
+      auto store_t = [&](int j, int i) {
         access(g.out_t, (tb + (long long)j * g.ldt + i) * es, 16, what);
         if (coverage) {
           std::vector<uint8_t>& cv = (g.out_t == g.out) ? cover : tcover;
           for (int e = 0; e < EPC; ++e) cv[tb + (long long)j * g.ldt + i + e]++;
+        }
+      };
+      if (es == 2) {
+        const int U = (t.bn / 16) * (t.bm / 32);
+        if (t.bn % 16 || t.bm % 32 || U % NW) fail(std::string(what) + ": mirror units do not split into waves");
+        for (int u = 0; u < U; ++u)
+          for (int lane = 0; lane < 64; ++lane) {
+            const MirrorLane ml = mirror_lane(u, lane, t.bn);
+            // every lane reads (the transposing read exchanges data in 16-lane groups)
+            for (int h = 0; h < 2; ++h) {
+              const long long e0 = (long long)ml.src_row[h] * SROW + ml.src_col;
+              if (ml.src_row[h] >= t.bm || ml.src_col + 3 >= t.bn || (e0 * es) % 8)
+                fail(std::string(what) + ": transposing read outside the staged tile or misaligned");
+              if ((e0 + 4) * es > (long long)LDS * 16) fail(std::string(what) + ": transposed read outside LDS");
+            }
+            if (ml.col >= t.bn || ml.row0 + 7 >= t.bm) fail(std::string(what) + ": mirror lane outside the tile");
+            const int j = j0 + ml.col, i = i0 + ml.row0;
+            if (j < g.N && i < g.M) store_t(j, i);
+          }
+        // the exchange model: lane t of a 16-lane group gets element t % 4 of
+        // the vectors read by lanes 4 e + t / 4; with the source addresses
+        // above that is column cb + t, rows row0 + 4 h + e
+        for (int u = 0; u < U; ++u)
+          for (int lane = 0; lane < 64; ++lane) {
+            const MirrorLane ml = mirror_lane(u, lane, t.bn);
+            const int t16 = lane & 15, g16 = lane & ~15;
+            for (int h = 0; h < 2; ++h)
+              for (int e = 0; e < 4; ++e) {
+                const MirrorLane src = mirror_lane(u, g16 + 4 * e + t16 / 4, t.bn);
+                const int row = src.src_row[h], col = src.src_col + t16 % 4;
+                if (row != ml.row0 + 4 * h + e || col != ml.col)
+                  fail(std::string(what) + ": transposing read does not deliver the mirror element");
+              }
+          }
+      } else {
+        const int RCH = t.bm / EPC;
+        for (int qd = 0; qd < t.bn * RCH; ++qd) {
+          const int jl = qd % t.bn, rc = qd / t.bn, j = j0 + jl, i = i0 + rc * EPC;
+          if (j >= g.N || i >= g.M) continue;
+          if (((long long)(rc * EPC + EPC - 1) * SROW + jl) * es + es > (long long)LDS * 16)
+            fail(std::string(what) + ": transposed read outside LDS");
+          store_t(j, i);
         }
       }
     }

@@ -590,18 +590,39 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
     *reinterpret_cast<uint4*>(O + (size_t)i * g.ldo + j) = val;
   }
 
-  // 3. transposed store: column jl of the tile, rows [EPC r .. +EPC)
+  // 3. transposed store (the mirror)
   if (g.out_t != nullptr && !diag_tile) {
     T* OT = reinterpret_cast<T*>(g.out_t) + (size_t)slice * g.ot_bs;
-    constexpr int RCH = BM / EPC;  // chunks per transposed row
-    for (int qd = tid; qd < BN * RCH; qd += NT) {
-      const int jl = qd % BN, rc = qd / BN;
-      const int j = j0 + jl, i = i0 + rc * EPC;
-      if (j >= g.N || i >= g.M) continue;
-      T tmp[EPC];
+    if constexpr (ES == 2) {
+      // transposing LDS reads; each wave store covers 16 output rows with
+      // 64 contiguous bytes each (mirror_lane)
+      static_assert(BN % 16 == 0 && BM % 32 == 0 && ((BN / 16) * (BM / 32)) % NW == 0, "mirror units");
+      for (int u = wave; u < (BN / 16) * (BM / 32); u += NW) {
+        const MirrorLane ml = mirror_lane(u, lane, BN);
+        uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) tmp[e] = S[(rc * EPC + e) * SROW + jl];
-      *reinterpret_cast<uint4*>(OT + (size_t)j * g.ldt + i) = *reinterpret_cast<const uint4*>(tmp);
+        for (int h = 0; h < 2; ++h) {
+          const short* src = reinterpret_cast<const short*>(S + ml.src_row[h] * SROW + ml.src_col);
+          const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)src);
+          w[2 * h] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+          w[2 * h + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+        }
+        const int j = j0 + ml.col, i = i0 + ml.row0;
+        if (j < g.N && i < g.M)
+          *reinterpret_cast<uint4*>(OT + (size_t)j * g.ldt + i) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    } else {
+      // fp32: column jl of the tile, rows [EPC r .. +EPC)
+      constexpr int RCH = BM / EPC;  // chunks per transposed row
+      for (int qd = tid; qd < BN * RCH; qd += NT) {
+        const int jl = qd % BN, rc = qd / BN;
+        const int j = j0 + jl, i = i0 + rc * EPC;
+        if (j >= g.N || i >= g.M) continue;
+        T tmp[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) tmp[e] = S[(rc * EPC + e) * SROW + jl];
+        *reinterpret_cast<uint4*>(OT + (size_t)j * g.ldt + i) = *reinterpret_cast<const uint4*>(tmp);
+      }
     }
   }
 }

@@ -217,6 +217,28 @@ NS_HD int nat_lane_byte_f32(int rb, int e, int lane, int rc) {
 }
 NS_HD constexpr int nat_step_bytes(int rc, int esize) { return (esize == 2 ? 16 : 8) * rc * 16; }
 
+// Mirror store of a staged bf16 tile (the transposes of its rows): one wave
+// instruction per unit u of 16 tile columns x 32 tile rows.  Lane l writes
+// 16 bytes of transposed row `col` (tile column 16 (u % (bn / 16)) + l % 16)
+// holding tile rows row0 .. row0 + 7, row0 = 8 (4 (u / (bn / 16)) + l / 16),
+// so one instruction covers 16 output rows with 64 contiguous bytes each.
+// It gathers them with two transposing LDS reads (ds_read_b64_tr_b16), for
+// which it addresses tile row src_row[h] at columns src_col .. + 3: in each
+// 16-lane group lane t then receives column cb + t of rows row0 + 4 h .. + 3.
+struct MirrorLane {
+  int col, row0, src_row[2], src_col;
+};
+NS_HD MirrorLane mirror_lane(int u, int lane, int bn) {
+  const int cgroups = bn / 16, cb = 16 * (u % cgroups), rq = u / cgroups, l16 = lane & 15;
+  MirrorLane m;
+  m.col = cb + l16;
+  m.row0 = 8 * (4 * rq + (lane >> 4));
+  m.src_row[0] = m.row0 + (l16 >> 2);
+  m.src_row[1] = m.row0 + 4 + (l16 >> 2);
+  m.src_col = cb + 4 * (l16 & 3);
+  return m;
+}
+
 // Operand layouts: K-contiguous rows (KCONT), the stored matrix read down its
 // columns (NAT), or a symmetric matrix of which only the lower block triangle
 // is stored (SYM: tiles of sym_tile rows, diagonal tiles whole).  A SYM
