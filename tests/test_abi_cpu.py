@@ -117,6 +117,9 @@ def boundscheck():
     "1 1 8 8 1", "1 1 8 2048 5", "1 4 2048 8 2", "1 1 136 136 5",
     "1 1 40 24 0",                           # zero steps
     "1 16 384 512 5", "1 2 1040 336 5",      # batched, tall, several tiles
+    # stacks whose Gram stores only its lower block triangle (256 and 128
+    # Gram tiles): every read of A must hit an element the Gram wrote
+    "1 400 264 520 2", "1 200 520 264 2",
 ])
 def test_launch_indexes_stay_in_bounds(boundscheck, case):
     r = subprocess.run([boundscheck] + case.split(), capture_output=True, text=True, timeout=600)

@@ -58,19 +58,22 @@ def test_small_shapes_bf16(shape):
     assert e.max() <= 1e-2
 
 
-@pytest.mark.parametrize("shape", [(400, 264, 520), (400, 520, 264)])
-def test_large_ragged_stack_bf16(shape):
-    # enough slices for the 256 x 256 Gram tile (ragged m = 264)
+@pytest.mark.parametrize("shape,gram_tile", [((400, 264, 520), 256), ((400, 520, 264), 256),
+                                             ((200, 264, 520), 128), ((200, 520, 264), 128)])
+def test_large_ragged_stack_bf16(shape, gram_tile):
+    # stacks large enough for the lower-triangle A (the poly reads the upper
+    # part from the transposed stored tiles), fed by the 256 (400 slices) or
+    # the 128 (200 slices) Gram tile, ragged m = 264, wide and tall
     dev = device()
-    x = gaussian(shape, 650 + shape[1], torch.bfloat16)
+    x = gaussian(shape, 650 + shape[0] + shape[1], torch.bfloat16)
     y = ns.orthogonalize(x.to(dev))
     torch.cuda.synchronize()
-    idx = [0, 137, 399]
+    idx = [0, 137, shape[0] - 1]
     ref = newton_schulz_batched(x[idx].double().numpy())
     e = rel_err(to64(y[idx]), ref)
     report({"case": f"large_ragged_bf16_{shape}", "max": float(e.max())})
     assert e.max() <= 1e-2
-    assert "gram: lower-tri tile=256x256" in ns.ns_query_last_config()
+    assert f"gram: lower-tri tile={gram_tile}x{gram_tile}" in ns.ns_query_last_config()
 
 
 @pytest.mark.parametrize("steps", [0, 1, 2, 3, 4, 5, 7])
