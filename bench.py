@@ -1,6 +1,7 @@
 """Benchmark of the batched Newton–Schulz orthogonalization on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--also NAME ...]
+    python bench.py --all-configs OUT_PREFIX      (every workload; writes OUT_PREFIX.md/.json)
 
 One step = one ns_orthogonalize call (normalisation + 5 quintic steps) over
 the whole workload, inputs already resident in HBM.  Prints ONE JSON line.
@@ -13,6 +14,10 @@ roofline    the dominant kernel (the update product) timed with HIP events
             FLOPs per launch / mean launch time, against the 2.5 PFLOP/s dense
             bf16 MFMA peak
 cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
+dense       the same method with dense PyTorch-ROCm bf16 matmuls (hipBLASLt),
+            timed on the same inputs: the comparator column of the pages'
+            dense-vs-symmetric table (bench only, not a library path)
+measured_peak  a plain 4096^3 bf16 torch.matmul (hipBLASLt) on this GPU
 """
 
 import argparse
@@ -83,6 +88,78 @@ def algorithmic_flops(batch, rows, cols):
     return {"gram": batch * m * (m + 1) * n, "poly": batch * m * m * (m + 1), "update": batch * 2 * m * m * n}
 
 
+def call_times(fn, steps):
+    """Per-call durations (ms) from HIP events around each call."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def spread(ts):
+    q = np.percentile(np.asarray(ts), [10, 50, 90])
+    return {"p10_ms": float(q[0]), "median_ms": float(q[1]), "p90_ms": float(q[2])}
+
+
+def dense_ns(x, steps=STEPS_NS, coeffs=None, eps=1e-7):
+    """The same method with dense bf16 matmuls in PyTorch-ROCm (hipBLASLt), as
+    in the dense routine the pages compare against: per slice X / (||X||_F +
+    eps), transposed if tall, then steps x (A = X Xᵀ, B = b A + c A A,
+    X = a X + B X).  A comparator only; the library never runs it."""
+    a, b, c = coeffs or ns.DEFAULT_COEFFS
+    X = x.reshape(-1, x.shape[-2], x.shape[-1])
+    tall = X.shape[-2] > X.shape[-1]
+    if tall:
+        X = X.transpose(-2, -1).contiguous()
+    nrm = torch.linalg.vector_norm(X, dim=(-2, -1), keepdim=True, dtype=torch.float32)
+    X = (X.float() / (nrm + eps)).to(x.dtype)
+    for _ in range(steps):
+        A = torch.matmul(X, X.transpose(-2, -1).contiguous())  # transposed operand made contiguous
+        B = b * A + c * torch.matmul(A, A)
+        X = a * X + torch.matmul(B, X)
+    if tall:
+        X = X.transpose(-2, -1).contiguous()
+    return X.reshape(x.shape)
+
+
+def time_dense(xg, steps, warmup):
+    for _ in range(warmup):
+        y = dense_ns(xg)
+    torch.cuda.synchronize()
+    ts = call_times(lambda: dense_ns(xg), steps)
+    y = dense_ns(xg)
+    torch.cuda.synchronize()
+    return {"ms_per_call": float(np.mean(ts)), **spread(ts)}, y
+
+
+def measured_peak(reps=20):
+    """TFLOP/s of a plain 4096^3 bf16 torch.matmul (hipBLASLt) on this GPU."""
+    n = 4096
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    ts = call_times(lambda: torch.matmul(a, b), reps)
+    return {"what": "torch.matmul bf16 4096x4096x4096 (hipBLASLt)",
+            "tflops": 2 * n ** 3 / (float(np.median(ts)) * 1e-3) / 1e12}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def time_workload(name, steps, warmup, kernel_mask):
     w = WORKLOADS[name]
     x = make_workload(name)
@@ -105,6 +182,8 @@ def time_workload(name, steps, warmup, kernel_mask):
     torch.cuda.synchronize()
     ns.ns_timing_enable(0)
     ms = start.elapsed_time(stop) / steps
+    ns.ns_timing_enable(0)
+    per_call = spread(call_times(lambda: ns.orthogonalize(xg, out=out), steps))
     kernels = {}
     for kind, kname in ns.KIND_NAMES.items():
         tot, n = ns.ns_timing_query(kind)
@@ -113,12 +192,12 @@ def time_workload(name, steps, warmup, kernel_mask):
     ns.ns_timing_reset()
     flops = dense_eq_flops(w.batch, w.rows, w.cols)
     eff = flops / (ms * 1e-3) / 1e12
-    return {"name": name, "shape": list(w.shape), "ms_per_call": ms, "eff_tflops": eff,
+    return {"name": name, "shape": list(w.shape), "ms_per_call": ms, **per_call, "eff_tflops": eff,
             "pct_dense_bf16_peak": 100.0 * eff / PEAK_BF16_TFLOPS, "kernels": kernels,
-            "config": ns.ns_query_last_config(), "x": x, "y": out}
+            "config": ns.ns_query_last_config(), "x": x, "xg": xg, "y": out}
 
 
-def cpu_baseline(name, y_gpu, budget_s):
+def cpu_baseline(name, y_gpu, budget_s, y_dense=None):
     """The fp64 oracle on whole slices of the workload, cycling through them,
     until ~budget_s seconds; each distinct slice is also compared with the GPU
     output."""
@@ -135,15 +214,18 @@ def cpu_baseline(name, y_gpu, budget_s):
     except Exception:  # noqa: BLE001
         cores = os.cpu_count() or 1
     ys = y_gpu.reshape(-1, w.rows, w.cols)
+    yd = y_dense.reshape(-1, w.rows, w.cols) if y_dense is not None else None
     t0 = time.perf_counter()
     done = 0
-    errs = []
+    errs, derrs = [], []
     while True:
         i = done % xs.shape[0]
         ref = newton_schulz_batched(xs[i:i + 1].double().numpy())[0]
         if done < xs.shape[0]:
             got = ys[i].double().cpu().numpy()
             errs.append(float(np.linalg.norm(got - ref) / np.linalg.norm(ref)))
+            if yd is not None:
+                derrs.append(float(np.linalg.norm(yd[i].double().cpu().numpy() - ref) / np.linalg.norm(ref)))
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -154,7 +236,90 @@ def cpu_baseline(name, y_gpu, budget_s):
             "sample": f"{done} oracle call(s) on {distinct} distinct of the {xs.shape[0]} slice(s) of {name} "
                       f"({w.rows}x{w.cols}), fp64 numpy, {dt:.1f} s",
             "seconds_per_slice": dt / done, "sample_rel_err_gpu_vs_oracle_max": max(errs),
-            "sample_rel_err_model_floor": rounding_floor(name, distinct)}
+            "sample_rel_err_model_floor": rounding_floor(name, distinct),
+            "sample_rel_err_dense_vs_oracle_max": max(derrs) if derrs else None, "cpu_model": cpu_model()}
+
+
+# the pages' H200 microbenchmark (ms per call, dense bf16 / QuACK symmetric)
+PAGES_H200_TABLE = {"lowrank64_4096x4096": (3.21, 2.71), "square_8192x8192": (25.5, 17.0),
+                    "mlp_4096x14336": (8.74, 7.07), "experts128_1536x2048": (35.9, 25.0),
+                    "experts128_2048x768": (12.9, 8.6), "experts32_7168x2048": (49.5, 33.0)}
+SAMPLES = {"experts16_1536x2048": [0, 7, 15], "experts128_1536x2048": [0, 63, 127],
+           "experts32_7168x2048": [0, 31], "experts128_2048x768": [0, 64, 127]}
+
+
+def all_configs(prefix, steps, warmup):
+    """Every workload: ms/call (and spread) of this build and of the dense
+    comparator, effective TFLOP/s against the spec and the measured peak, and
+    both outputs' relative error vs the fp64 oracle on sampled slices beside
+    the rounding-model floor.  Writes prefix.json and prefix.md."""
+    from oracle import newton_schulz  # the error columns only
+
+    peak = measured_peak()
+    print(json.dumps({"measured_peak": peak}), flush=True)
+    rows = []
+    oracle_cache = {}
+    runs = [(n, torch.bfloat16) for n in WORKLOADS] + [("iid_256x512", torch.float32)]
+    for name, dtype in runs:
+        w = WORKLOADS[name]
+        x0 = make_workload(name)  # the oracle reads this tensor (the fp32 original for a bf16 run of it)
+        x = x0.to(dtype)
+        xg = x.to("cuda:0")
+        out = torch.empty_like(xg)
+        for _ in range(warmup):
+            ns.orthogonalize(xg, out=out)
+        torch.cuda.synchronize()
+        ts = call_times(lambda: ns.orthogonalize(xg, out=out), steps)
+        d, yd = time_dense(xg, max(3, steps // 2), 2)
+        flops = dense_eq_flops(w.batch, w.rows, w.cols)
+        ms = float(np.mean(ts))
+        eff = flops / (ms * 1e-3) / 1e12
+        xs, ys, yds = (t.reshape(-1, w.rows, w.cols) for t in (x0, out, yd))
+        errs, derrs, osec = [], [], []
+        for i in SAMPLES.get(name, [0]):
+            # the transposed MLP weight reuses its transpose's oracle: NS(Xᵀ) = NS(X)ᵀ
+            key = (name.replace("mlp_14336x4096", "mlp_4096x14336"), i)
+            t0 = time.perf_counter()
+            if key[0] != name and key in oracle_cache:
+                ref = oracle_cache[key].T
+            else:
+                if (name, i) not in oracle_cache:
+                    oracle_cache[(name, i)] = newton_schulz(xs[i].double().numpy())
+                ref = oracle_cache[(name, i)]
+            osec.append(time.perf_counter() - t0)
+            for y, e in ((ys, errs), (yds, derrs)):
+                g = y[i].double().cpu().numpy()
+                e.append(float(np.linalg.norm(g - ref) / np.linalg.norm(ref)))
+        peak_spec = PEAK_BF16_TFLOPS if dtype == torch.bfloat16 else PEAK_F32_TFLOPS
+        row = {"workload": name, "shape": list(w.shape), "dtype": "bf16" if dtype == torch.bfloat16 else "fp32",
+               "ms_per_call": ms, **spread(ts), "eff_tflops": eff, "pct_spec_peak": 100 * eff / peak_spec,
+               "pct_measured_peak": 100 * eff / peak["tflops"] if dtype == torch.bfloat16 else None,
+               "dense_ms_per_call": d["ms_per_call"], "speedup_vs_dense": d["ms_per_call"] / ms,
+               "err_max": max(errs), "err_mean": float(np.mean(errs)), "dense_err_max": max(derrs),
+               "model_floor": rounding_floor(name, 10 ** 9) if dtype == torch.bfloat16 else None,
+               "sampled_slices": SAMPLES.get(name, [0]), "oracle_s_per_slice": float(np.mean(osec)),
+               "pages_h200_dense_quack_ms": PAGES_H200_TABLE.get(name)}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        del xg, out, yd
+        torch.cuda.empty_cache()
+    host = {"cpu_model": cpu_model(), "cores": len(os.sched_getaffinity(0))}
+    with open(prefix + ".json", "w") as f:
+        json.dump({"measured_peak": peak, "host": host, "rows": rows}, f, indent=1)
+    lines = ["| workload | dtype | ms/call (p10-p90) | eff. TFLOP/s | % spec peak | % measured peak | dense ms | "
+             "speedup vs dense | err max / mean | dense err | model floor | oracle s/slice | H200 dense / QuACK ms |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        pm = f"{r['pct_measured_peak']:.1f}%" if r["pct_measured_peak"] is not None else "-"
+        fl = f"{r['model_floor']:.2e}" if r["model_floor"] is not None else "-"
+        h2 = "{} / {}".format(*r["pages_h200_dense_quack_ms"]) if r["pages_h200_dense_quack_ms"] else "-"
+        lines.append(f"| {r['workload']} | {r['dtype']} | {r['ms_per_call']:.3f} ({r['p10_ms']:.3f}-{r['p90_ms']:.3f}) | "
+                     f"{r['eff_tflops']:.0f} | {r['pct_spec_peak']:.1f}% | {pm} | {r['dense_ms_per_call']:.3f} | "
+                     f"{r['speedup_vs_dense']:.2f}x | {r['err_max']:.2e} / {r['err_mean']:.2e} | "
+                     f"{r['dense_err_max']:.2e} | {fl} | {r['oracle_s_per_slice']:.1f} | {h2} |")
+    with open(prefix + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
 
 
 def rounding_floor(name, n):
@@ -178,6 +343,10 @@ def main():
     ap.add_argument("--also", nargs="*", default=["experts128_1536x2048"])
     ap.add_argument("--kernel-timing", choices=["dominant", "all", "none"], default="dominant")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time, at least (0: skip)")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense PyTorch comparator")
+    ap.add_argument("--all-configs", metavar="OUT_PREFIX",
+                    help="time and check every workload (this build's and the dense comparator's error vs "
+                         "the oracle on sampled slices), write OUT_PREFIX.md and OUT_PREFIX.json, and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 64 MiB device copy three times (the reference that scales "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE into bytes) and exit")
@@ -200,9 +369,24 @@ def main():
         print(json.dumps({"copy_bytes": src.numel(), "reads": src.numel(), "writes": src.numel()}))
         return
 
+    if args.all_configs:
+        all_configs(args.all_configs, args.steps, args.warmup)
+        return
+
     mask = {"dominant": 1 << ns.NS_KIND_UPDATE, "all": 0x1F, "none": 0}[args.kernel_timing]
     main_run = time_workload(args.workload, args.steps, args.warmup, mask)
     extra = [time_workload(n, args.steps, args.warmup, mask) for n in args.also if n != args.workload]
+    peak = measured_peak()
+    y_dense = None
+    for r in [main_run] + extra:
+        r["pct_measured_peak"] = 100.0 * r["eff_tflops"] / peak["tflops"]
+        if not args.no_dense:
+            d, yd = time_dense(r["xg"], max(3, args.steps // 2), 2)
+            r["dense"] = {**d, "eff_tflops": r["eff_tflops"] * r["ms_per_call"] / d["ms_per_call"],
+                          "speedup_of_this_build": d["ms_per_call"] / r["ms_per_call"]}
+            if r is main_run:
+                y_dense = yd
+            del yd
 
     w = WORKLOADS[args.workload]
     algo = algorithmic_flops(w.batch, w.rows, w.cols)
@@ -219,14 +403,16 @@ def main():
 
     cpu = None
     if args.cpu_budget > 0:
-        cpu = cpu_baseline(args.workload, main_run["y"], args.cpu_budget)
+        cpu = cpu_baseline(args.workload, main_run["y"], args.cpu_budget, y_dense)
 
     flops = dense_eq_flops(w.batch, w.rows, w.cols)
     pages_ms = PAGES_H200_MS.get(args.workload)
     vs = (main_run["eff_tflops"] / (flops / (pages_ms * 1e-3) / 1e12)) if pages_ms else None
 
     def summary(r):
-        return {k: r[k] for k in ("name", "shape", "ms_per_call", "eff_tflops", "pct_dense_bf16_peak", "kernels")}
+        keys = ("name", "shape", "ms_per_call", "p10_ms", "median_ms", "p90_ms", "eff_tflops", "pct_dense_bf16_peak",
+                "pct_measured_peak", "dense", "kernels")
+        return {k: r[k] for k in keys if k in r}
 
     line = {
         "metric": "NS ms/call + effective bf16 TFLOP/s (% MFMA peak) at 4096^2 and 128x1536x2048",
@@ -244,6 +430,7 @@ def main():
         "config": {"workload": args.workload, "shape": list(w.shape), "ns_steps": STEPS_NS,
                    "coeffs": list(ns.DEFAULT_COEFFS), "pct_dense_bf16_peak": main_run["pct_dense_bf16_peak"],
                    "kernel_config": main_run["config"]},
+        "measured_peak": peak,
         "workloads": [summary(main_run)] + [summary(r) for r in extra],
         "baseline_context": {"hardware": "1x H200", "ms_per_call": pages_ms,
                              "source": "prime-rl PR #3873, NS microbenchmark table (QuACK symmetric GEMM)"},

@@ -69,6 +69,9 @@ WORKLOADS = {
                  "seed-4 generator, second draw: Z[32,7168,2048] iid N(0,1)"),
         Workload("square_8192x8192", (8192, 8192), torch.bfloat16, 4,
                  "seed-4 generator, third draw: Z[8192,8192] iid N(0,1)"),
+        Workload("experts128_2048x768", (128, 2048, 768), torch.bfloat16, 5,
+                 "seed 5: Z[128,2048,768] iid N(0,1) (the pages' sixth microbenchmark "
+                 "shape; tall, Gram 768 x 768)"),
     ]
 }
 
@@ -122,4 +125,6 @@ def make_workload(name):
         return (z * s.view(16, 1, 1)).to(torch.bfloat16)
     if name in ("experts128_1536x2048", "experts32_7168x2048", "square_8192x8192"):
         return _seed4_stack(name)
+    if name == "experts128_2048x768":
+        return gaussian(w.shape, w.seed, torch.bfloat16)
     raise KeyError(name)

@@ -4,7 +4,10 @@ fp64 oracle on each named workload (sampled slices for stacks).
 Calls only oracle/ (ns_oracle and the rounding model) and the seeded input
 recipes.  Run from the repository root:
 
-    python tests/golden/make_rounding_floor.py
+    python tests/golden/make_rounding_floor.py [NAME ...]
+
+With names, only those workloads are recomputed and merged into the existing
+file.
 """
 
 import json
@@ -23,19 +26,24 @@ from oracle import newton_schulz  # noqa: E402
 from oracle.rounding_model import ns_bf16_model  # noqa: E402
 
 SAMPLES = {"experts16_1536x2048": [0, 7, 15], "experts128_1536x2048": [0, 63, 127],
-           "experts32_7168x2048": [0, 31]}
+           "experts32_7168x2048": [0, 31], "experts128_2048x768": [0, 64, 127]}
+NAMES = ["iid_256x512", "lowrank64_4096x4096", "mlp_4096x14336", "experts16_1536x2048", "experts128_1536x2048",
+         "experts32_7168x2048", "square_8192x8192", "experts128_2048x768"]
 
 
 def rel(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
 
-def main():
+def main(names):
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "rounding_floor.json")
     out = {"what": "relative Frobenius error vs the fp64 oracle of the CPU bf16 rounding model "
                    "(oracle/rounding_model.py); 'diag' is the placement the HIP kernels use",
            "workloads": {}}
-    for name in ["iid_256x512", "lowrank64_4096x4096", "mlp_4096x14336", "experts16_1536x2048",
-                 "experts128_1536x2048", "experts32_7168x2048", "square_8192x8192"]:
+    if names:
+        with open(path) as f:
+            out["workloads"] = json.load(f)["workloads"]
+    for name in names or NAMES:
         t0 = time.time()
         w = WORKLOADS[name]
         x = make_workload(name)
@@ -51,9 +59,9 @@ def main():
         print(name, rec, f"{time.time() - t0:.0f}s", flush=True)
     # the transposed MLP weight has the same floor (NS(Xᵀ) = NS(X)ᵀ)
     out["workloads"]["mlp_14336x4096"] = out["workloads"]["mlp_4096x14336"]
-    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "rounding_floor.json"), "w") as f:
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
 
 
 if __name__ == "__main__":
-    main()
+    main(sys.argv[1:])

@@ -30,7 +30,7 @@ pytestmark = pytest.mark.gpu
 
 FLOOR = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "rounding_floor.json")))["workloads"]
 SAMPLES = {"experts16_1536x2048": [0, 7, 15], "experts128_1536x2048": [0, 63, 127],
-           "experts32_7168x2048": [0, 31]}
+           "experts32_7168x2048": [0, 31], "experts128_2048x768": [0, 64, 127]}
 FLOORED = {"lowrank64_4096x4096", "mlp_4096x14336", "mlp_14336x4096"}
 
 _oracle_cache = {}
@@ -63,7 +63,7 @@ def run(name, dtype):
 
 
 NAMES = ["lowrank64_4096x4096", "mlp_4096x14336", "mlp_14336x4096", "experts16_1536x2048",
-         "experts128_1536x2048", "experts32_7168x2048", "square_8192x8192"]
+         "experts128_1536x2048", "experts32_7168x2048", "square_8192x8192", "experts128_2048x768"]
 
 
 @pytest.mark.parametrize("name", NAMES)
