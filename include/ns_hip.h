@@ -55,8 +55,8 @@ typedef enum {
   NS_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, ns_steps < 0,
                              rows*cols >= 2^31, partial overlap in/out    */
   NS_ERR_DTYPE = 2,       /* dtype is not NS_DTYPE_F32 / NS_DTYPE_BF16    */
-  NS_ERR_ALIGNMENT = 3,   /* rows or cols not a multiple of 8, or a pointer
-                             not 16-byte aligned (16-byte rows)           */
+  NS_ERR_ALIGNMENT = 3,   /* a pointer not 16-byte aligned; for the stage
+                             exports also rows or cols not a multiple of 8 */
   NS_ERR_ARCH = 4,        /* current device is not gfx950                 */
   NS_ERR_OOM = 5,         /* workspace allocation failed                  */
   NS_ERR_HIP = 6          /* a HIP runtime call or launch failed;
@@ -78,7 +78,12 @@ enum {
  *             overlap is NS_ERR_INVALID_ARG.  out always has the input's
  *             orientation (tall inputs are NOT returned transposed).
  *   batch     number of independent slices (0..65535; 0 enqueues nothing).
- *   rows,cols slice shape, each > 0 and a multiple of 8.
+ *   rows,cols slice shape, each > 0.  When rows or cols is not a multiple
+ *             of 8 the call zero-pads each slice to multiples of 8 in the
+ *             workspace, runs on the padded copy and copies the caller's
+ *             block back (zero rows and columns add only zero singular
+ *             values, so the result is NS of the caller's matrix); the pad
+ *             and unpad passes cost two extra copies of the stack.
  *   dtype     NS_DTYPE_F32 or NS_DTYPE_BF16.
  *   ns_steps  number of quintic steps (>= 0; 0 returns X / (||X||_F + eps)).
  *   a, b, c   quintic coefficients (Muon's usual: 3.4445, -4.7750, 2.0315).
@@ -137,8 +142,9 @@ int ns_timing_reset(void);
 int ns_timing_query(int kind, double* total_ms, int64_t* launches);
 
 /* ---- single stages (the same kernels ns_orthogonalize runs) ------------- */
-/* Shapes: a slice of x is rows x cols; m = min(rows, cols).  The Gram side is
- * the short one: A = X Xᵀ when rows <= cols, A = Xᵀ X when rows > cols. */
+/* Shapes: a slice of x is rows x cols, both multiples of 8 (the stages do
+ * not pad); m = min(rows, cols).  The Gram side is the short one: A = X Xᵀ
+ * when rows <= cols, A = Xᵀ X when rows > cols. */
 
 /* X0 = x / (||x||_F + 1e-7) per slice, same shape, layout and dtype.
  * norms (optional, may be NULL): fp32 [batch] receives ||x||_F per slice.

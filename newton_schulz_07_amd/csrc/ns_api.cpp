@@ -50,13 +50,16 @@ int check_dtype(int dtype) {
   return NS_OK;
 }
 
-int check_shape(int64_t batch, int64_t rows, int64_t cols) {
+// any_dims: rows and cols need not be multiples of 8 (ns_orthogonalize pads
+// such shapes; the stage exports do not)
+int check_shape(int64_t batch, int64_t rows, int64_t cols, bool any_dims = false) {
   if (batch < 0) return fail(NS_ERR_INVALID_ARG, "batch must be >= 0");
   if (rows <= 0 || cols <= 0) return fail(NS_ERR_INVALID_ARG, "rows and cols must be > 0");
-  if (rows % 8 != 0 || cols % 8 != 0)
+  if (!any_dims && (rows % 8 != 0 || cols % 8 != 0))
     return fail(NS_ERR_ALIGNMENT, "rows and cols must be multiples of 8 (16-byte rows), got " +
                                       std::to_string(rows) + "x" + std::to_string(cols));
-  if (rows * cols >= (int64_t(1) << 29))
+  if (rows >= (int64_t(1) << 29) || cols >= (int64_t(1) << 29) ||
+      ns::round_up8(rows) * ns::round_up8(cols) >= (int64_t(1) << 29))
     return fail(NS_ERR_INVALID_ARG, "a slice must hold fewer than 2^29 elements (2 GiB of fp32)");
   if (batch > 65535) return fail(NS_ERR_INVALID_ARG, "batch must be <= 65535");
   return NS_OK;
@@ -220,11 +223,14 @@ void record_config(const Plan& p, int steps) {
                 tp.cpr * 16, tp.st, p.tall ? "X*C" : "C*X", tr.bm, tr.bn, tr.wm, tr.wn, tr.cpr * 16, tr.st,
                 p.tall ? "rows" : "columns(transposed-read)");
   t_cfg = buf;
+  if (p.padded)
+    t_cfg += " | zero-padded from " + std::to_string(p.urows) + "x" + std::to_string(p.ucols) + " to " +
+             std::to_string(p.rows) + "x" + std::to_string(p.cols);
 }
 
-int common_checks(int64_t batch, int64_t rows, int64_t cols, int dtype) {
+int common_checks(int64_t batch, int64_t rows, int64_t cols, int dtype, bool any_dims = false) {
   if (int s = check_dtype(dtype)) return s;
-  return check_shape(batch, rows, cols);
+  return check_shape(batch, rows, cols, any_dims);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -242,7 +248,7 @@ extern "C" {
 int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows, int64_t cols, int dtype,
                      int ns_steps, float a, float b, float c, void* stream) {
   t_err.clear();
-  if (int s = common_checks(batch, rows, cols, dtype)) return s;
+  if (int s = common_checks(batch, rows, cols, dtype, true)) return s;
   if (ns_steps < 0) return fail(NS_ERR_INVALID_ARG, "ns_steps must be >= 0");
   if (int s = check_ptr(in, "in")) return s;
   if (int s = check_ptr(out, "out")) return s;
@@ -263,6 +269,17 @@ int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows, int
   float* dc = reinterpret_cast<float*>(ws + p.off_dc);
   float* part = reinterpret_cast<float*>(ws + p.off_part);
 
+  // odd shapes: the method runs on zero-padded copies (see ns_plan.h)
+  const void* uin = in;
+  void* uout = out;
+  if (p.padded) {
+    const ns::PadArgs pa = ns::pad_args(p, uin, ws + p.off_pin, true);
+    if (int s = check_hip(ns::launch_pad(dtype, pa, st), "pad launch")) return s;
+    in = ws + p.off_pin;
+    out = ws + p.off_pout;
+  }
+  const size_t pbytes = (size_t)p.batch * p.rows * p.cols * esize(dtype);
+
   const bool fold = ns::fold_normalisation(ns_steps);
   const bool copy_in = ns::input_copy_needed(ns_steps, in == out);
   auto buf = [&](int s) -> const void* {
@@ -274,7 +291,7 @@ int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows, int
   // folded: sums of squares only; otherwise (no step) X0 = x / (||x|| + eps)
   if (int s = run_normalize(in, fold ? nullptr : wbuf(0), nullptr, p, part, st)) return s;
   if (copy_in)  // out == in, odd steps: X_0 is a copy of the input (see ns_plan.h)
-    if (int s = check_hip(hipMemcpyAsync(xtmp, in, bytes, hipMemcpyDeviceToDevice, st), "input copy")) return s;
+    if (int s = check_hip(hipMemcpyAsync(xtmp, in, pbytes, hipMemcpyDeviceToDevice, st), "input copy")) return s;
   for (int s = 1; s <= ns_steps; ++s) {
     const float* dn = (fold && s == 1) ? part : nullptr;  // partial sums of squares -> ||x||_F
     // the poly reads A as its lower block triangle when it can (no mirror)
@@ -282,12 +299,16 @@ int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows, int
     if (int e = run_poly(oa, da, oc, dc, p, a, b, c, st)) return e;
     if (int e = run_update(buf(s - 1), oc, dc, wbuf(s), p, st, dn)) return e;
   }
+  if (p.padded) {
+    const ns::PadArgs pa = ns::pad_args(p, out, uout, false);
+    if (int s = check_hip(ns::launch_pad(dtype, pa, st), "unpad launch")) return s;
+  }
   record_config(p, ns_steps);
   return NS_OK;
 }
 
 size_t ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int dtype) {
-  if (check_dtype(dtype) != NS_OK || check_shape(batch, rows, cols) != NS_OK) return 0;
+  if (check_dtype(dtype) != NS_OK || check_shape(batch, rows, cols, true) != NS_OK) return 0;
   return make_plan(batch, rows, cols, dtype).total;
 }
 
@@ -314,7 +335,7 @@ const char* ns_status_string(int status) {
     case NS_OK: return "NS_OK";
     case NS_ERR_INVALID_ARG: return "NS_ERR_INVALID_ARG: invalid argument";
     case NS_ERR_DTYPE: return "NS_ERR_DTYPE: unsupported dtype";
-    case NS_ERR_ALIGNMENT: return "NS_ERR_ALIGNMENT: dims must be multiples of 8, pointers 16-byte aligned";
+    case NS_ERR_ALIGNMENT: return "NS_ERR_ALIGNMENT: pointers must be 16-byte aligned (stage exports: dims multiples of 8)";
     case NS_ERR_ARCH: return "NS_ERR_ARCH: device is not gfx950";
     case NS_ERR_OOM: return "NS_ERR_OOM: workspace allocation failed";
     case NS_ERR_HIP: return "NS_ERR_HIP: HIP runtime error";

@@ -457,16 +457,47 @@ void replay_norm(const NormArgs& g, int batch, bool scale, const char* what) {
     }
 }
 
+// Pad or unpad (mirrors pad_kernel): destination element e of every slice,
+// first and last of each destination row, reads and writes in bounds.
+void replay_pad(const PadArgs& g, int es, const char* what) {
+  const long long dr = g.to_padded ? g.rows : g.urows, dc = g.to_padded ? g.cols : g.ucols;
+  if (g.urows > g.rows || g.ucols > g.cols || g.rows % 8 || g.cols % 8) fail(std::string(what) + ": bad padded shape");
+  for (long long b = 0; b < g.batch; ++b)
+    for (long long i = 0; i < dr; ++i)
+      for (long long j : {0LL, dc - 1}) {
+        const long long e = (b * dr + i) * dc + j;
+        access(g.dst, e * es, es, what);
+        if (g.to_padded) {
+          if (i < g.urows && j < g.ucols) access(g.src, ((b * g.urows + i) * g.ucols + j) * es, es, what);
+        } else {
+          access(g.src, ((b * g.rows + i) * g.cols + j) * es, es, what);
+        }
+      }
+}
+
 // Replays one ns_orthogonalize call as the driver sequences it.
-void replay_call(int dtype, long long batch, long long rows, long long cols, int steps, bool alias) {
+void replay_call(int dtype, long long batch, long long urows, long long ucols, int steps, bool alias) {
   g_bufs.clear();
   g_written.clear();
-  const Plan p = make_plan(batch, rows, cols, dtype);
+  const Plan p = make_plan(batch, urows, ucols, dtype);
+  const long long rows = p.rows, cols = p.cols;  // padded to multiples of 8
   const int es = (int)elem_size(dtype);
+  const size_t ubytes = (size_t)batch * urows * ucols * es;
   const size_t xbytes = (size_t)batch * rows * cols * es;
   const size_t mm = (size_t)batch * p.m * p.m * es;
-  void* in = reg(uintptr_t(1) << 44, "in", xbytes);
-  void* out = alias ? in : reg(uintptr_t(2) << 44, "out", xbytes);
+  void* uin = reg(uintptr_t(1) << 44, "in", ubytes);
+  void* uout = alias ? uin : reg(uintptr_t(2) << 44, "out", ubytes);
+  void* in = uin;
+  void* out = uout;
+  if (p.padded) {  // the method runs on zero-padded workspace copies
+    if (p.off_pout - p.off_pin < xbytes || p.total - p.off_pout < xbytes) fail("workspace plan: padded buffers");
+    in = reg(uintptr_t(9) << 44, "padded in", xbytes);
+    out = reg(uintptr_t(10) << 44, "padded out", xbytes);
+    replay_pad(pad_args(p, uin, in, true), es, "pad");
+  } else if (ubytes != xbytes) {
+    fail("unpadded plan with a padded size");
+  }
+  alias = in == out;
   void* xtmp = reg(uintptr_t(3) << 44, "xtmp", xbytes);
   void* oa = reg(uintptr_t(4) << 44, "oa", mm);
   void* oc = reg(uintptr_t(5) << 44, "oc", mm);
@@ -498,6 +529,8 @@ void replay_call(int dtype, long long batch, long long rows, long long cols, int
     g = update_args(p, buf(s - 1), oc, dc, wbuf(s), &kind, dn);
     replay_gemm(g, kind, dtype, cov, "update");
   }
+  if (steps >= 1 && wbuf(steps) != out) fail("the last step does not write the result buffer");
+  if (p.padded) replay_pad(pad_args(p, out, uout, false), es, "unpad");
 }
 
 }  // namespace

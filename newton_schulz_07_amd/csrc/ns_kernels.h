@@ -12,5 +12,6 @@ namespace ns {
 hipError_t launch_gemm(int dtype, const StageKind& k, const GemmArgs& g, hipStream_t st);
 hipError_t launch_sumsq(int dtype, const NormArgs& g, int batch, hipStream_t st);
 hipError_t launch_scale(int dtype, const NormArgs& g, int batch, hipStream_t st);
+hipError_t launch_pad(int dtype, const PadArgs& g, hipStream_t st);
 
 }  // namespace ns

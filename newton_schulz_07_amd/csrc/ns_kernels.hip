@@ -713,6 +713,28 @@ __global__ __launch_bounds__(kNormThreads) void scale_kernel(const NormArgs g) {
   for (long long v = v0 + threadIdx.x; v < v1; v += kNormThreads) yv[v] = scale16(xv[v], inv, T());
 }
 
+// --------------------------------------------------- padding (odd shapes)
+
+// One element of the destination per thread (grid-stride): pad writes the
+// whole padded slice (zeros outside the caller's rows x cols), unpad reads
+// the caller's block back out of the padded result.
+template <typename T>
+__global__ __launch_bounds__(256) void pad_kernel(const PadArgs g) {
+  const T* src = reinterpret_cast<const T*>(g.src);
+  T* dst = reinterpret_cast<T*>(g.dst);
+  const long long dr = g.to_padded ? g.rows : g.urows, dc = g.to_padded ? g.cols : g.ucols;
+  const long long total = g.batch * dr * dc;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const long long b = e / (dr * dc), r = e % (dr * dc);
+    const long long i = r / dc, j = r % dc;
+    if (g.to_padded)
+      dst[e] = (i < g.urows && j < g.ucols) ? src[(b * g.urows + i) * g.ucols + j] : T(0.0f);
+    else
+      dst[e] = src[(b * g.rows + i) * g.cols + j];
+  }
+}
+
 // ------------------------------------------------------------- launchers
 
 template <typename T, int MODE, int CLS, int PL, int QL>
@@ -762,6 +784,15 @@ static hipError_t dispatch_mode(const StageKind& k, const GemmArgs& g, hipStream
 hipError_t launch_gemm(int dtype, const StageKind& k, const GemmArgs& g, hipStream_t st) {
   if (dtype == 1) return dispatch_mode<bf16>(k, g, st);
   return dispatch_mode<float>(k, g, st);
+}
+
+hipError_t launch_pad(int dtype, const PadArgs& g, hipStream_t st) {
+  const long long total = g.batch * (g.to_padded ? g.rows * g.cols : g.urows * g.ucols);
+  const long long want = (total + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 65536 ? (want > 0 ? want : 1) : 65536);
+  if (dtype == 1) hipLaunchKernelGGL(pad_kernel<bf16>, dim3(blocks), dim3(256), 0, st, g);
+  else hipLaunchKernelGGL(pad_kernel<float>, dim3(blocks), dim3(256), 0, st, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_sumsq(int dtype, const NormArgs& g, int batch, hipStream_t st) {

@@ -19,17 +19,31 @@ inline size_t ws_align(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAli
 inline int tiles_of(int64_t extent, int tile) { return (int)((extent + tile - 1) / tile); }
 
 // One call on [batch, rows, cols].  The Gram side is m = min(rows, cols).
+// A shape whose rows or cols is not a multiple of 8 runs on a zero-padded
+// copy (rows and cols rounded up to 8): zero rows and columns only add zero
+// singular values, which every step maps to zero, so NS of [X 0; 0 0] is
+// [NS(X) 0; 0 0] and the Frobenius norm is unchanged.  rows / cols are then
+// the padded sizes, urows / ucols the caller's, and the workspace holds the
+// padded input and output.
 struct Plan {
   int64_t batch, rows, cols, m, n;
   bool tall;
   int dtype;
   int norm_chunks;
+  bool padded;
+  int64_t urows, ucols;
   // workspace offsets (bytes)
-  size_t off_xtmp, off_oa, off_oc, off_da, off_dc, off_part, total;
+  size_t off_xtmp, off_oa, off_oc, off_da, off_dc, off_part, off_pin, off_pout, total;
 };
 
-inline Plan make_plan(int64_t batch, int64_t rows, int64_t cols, int dtype) {
+inline int64_t round_up8(int64_t v) { return (v + 7) / 8 * 8; }
+
+inline Plan make_plan(int64_t batch, int64_t urows, int64_t ucols, int dtype) {
+  const int64_t rows = round_up8(urows), cols = round_up8(ucols);
   Plan p{};
+  p.padded = rows != urows || cols != ucols;
+  p.urows = urows;
+  p.ucols = ucols;
   p.batch = batch;
   p.rows = rows;
   p.cols = cols;
@@ -53,8 +67,26 @@ inline Plan make_plan(int64_t batch, int64_t rows, int64_t cols, int dtype) {
   off += ws_align((size_t)batch * p.m * 4);
   p.off_part = off;
   off += ws_align((size_t)batch * p.norm_chunks * 4);
+  p.off_pin = p.off_pout = off;
+  if (p.padded) {
+    off += ws_align((size_t)batch * rows * cols * es);
+    p.off_pout = off;
+    off += ws_align((size_t)batch * rows * cols * es);
+  }
   p.total = off;
   return p;
+}
+
+// Zero-padded copy in (pad) or the caller's block out (unpad) of a padded
+// plan: one thread per element of the destination.
+struct PadArgs {
+  const void* src;
+  void* dst;
+  long long batch, urows, ucols, rows, cols;  // caller's and padded slice sizes
+  bool to_padded;                            // pad (true) or unpad (false)
+};
+inline PadArgs pad_args(const Plan& p, const void* src, void* dst, bool to_padded) {
+  return PadArgs{src, dst, p.batch, p.urows, p.ucols, p.rows, p.cols, to_padded};
 }
 
 // The iterate X_s (s = 0 after normalisation) is held in `out` when

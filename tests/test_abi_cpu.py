@@ -49,8 +49,6 @@ def call(batch=1, rows=256, cols=512, dtype=1, steps=5, inp=FAKE_IN, out=FAKE_OU
     (dict(rows=16384, cols=32768), 1),     # 2^29 elements: over the 2 GiB fp32 slice limit
     (dict(dtype=2), 2),
     (dict(dtype=-1), 2),
-    (dict(rows=260), 3),                   # not a multiple of 8
-    (dict(cols=100), 3),
     (dict(inp=FAKE_IN + 8), 3),            # not 16-byte aligned
     (dict(out=FAKE_IN + 256 * 512), 1),    # partial overlap with in
 ])
@@ -59,6 +57,16 @@ def test_argument_errors_are_reported_before_any_launch(kwargs, status):
     assert st == status
     assert ns.lib().ns_last_error().decode() != ""
     assert ns.lib().ns_status_string(st).decode().startswith("NS_ERR")
+
+
+@pytest.mark.parametrize("rows,cols", [(260, 512), (256, 100), (1, 1), (9, 13)])
+def test_dims_not_multiple_of_8_pass_the_argument_checks(rows, cols):
+    # ns_orthogonalize pads such shapes (stage exports still refuse them);
+    # without a GPU the call gets as far as the device query
+    st = call(rows=rows, cols=cols)
+    assert st not in (1, 2, 3), ns.lib().ns_last_error().decode()
+    pr, pc = -(-rows // 8) * 8, -(-cols // 8) * 8
+    assert ns.ns_workspace_bytes(2, rows, cols, 1) >= ns.ns_workspace_bytes(2, pr, pc, 1) + 2 * 2 * pr * pc * 2
 
 
 def test_empty_batch_is_a_no_op():
@@ -86,7 +94,8 @@ def test_workspace_bytes():
     assert ws >= b * r * c * 2 + 2 * b * r * r * 2 + 2 * b * r * 4
     assert ws < 1.01 * (b * r * c * 2 + 2 * b * r * r * 2) + (1 << 20)
     assert L.ns_workspace_bytes(1, 14336, 4096, 1) == L.ns_workspace_bytes(1, 4096, 14336, 1)
-    assert L.ns_workspace_bytes(1, 10, 16, 1) == 0  # invalid shape
+    assert L.ns_workspace_bytes(1, 10, 16, 1) > L.ns_workspace_bytes(1, 16, 16, 1)  # padded copies
+    assert L.ns_workspace_bytes(1, 0, 16, 1) == 0  # invalid shape
     assert L.ns_workspace_bytes(1, 16, 16, 7) == 0  # invalid dtype
 
 
@@ -120,6 +129,8 @@ def boundscheck():
     # stacks whose Gram stores only its lower block triangle (256 and 128
     # Gram tiles): every read of A must hit an element the Gram wrote
     "1 400 264 520 2", "1 200 520 264 2",
+    # rows or cols not a multiple of 8: zero-padded copies in and out
+    "1 3 100 37 3", "0 2 33 17 2", "1 1 1 1 2", "1 2 9 2051 1", "0 1 5 3 0",
 ])
 def test_launch_indexes_stay_in_bounds(boundscheck, case):
     r = subprocess.run([boundscheck] + case.split(), capture_output=True, text=True, timeout=600)

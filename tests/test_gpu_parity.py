@@ -12,6 +12,7 @@ import torch
 import newton_schulz_07_amd as ns
 from ns_inputs import gaussian, make_workload
 from oracle import newton_schulz, newton_schulz_batched
+from oracle.rounding_model import ns_bf16_model
 from tests.gpu_util import device, rel_err, report, to64
 
 pytestmark = pytest.mark.gpu
@@ -162,9 +163,46 @@ def test_deterministic_and_batch_invariant(dtype):
 def test_errors_raise_and_do_not_fall_back():
     dev = device()
     with pytest.raises(ns.NSError):
-        ns.orthogonalize(torch.zeros(12, 16, device=dev))  # 12 is not a multiple of 8
+        ns.ns_stage_gram(torch.zeros(12, 16, device=dev))  # stage exports need multiples of 8
     with pytest.raises(TypeError):
         ns.orthogonalize(torch.zeros(16, 16, device=dev, dtype=torch.float16))
+
+
+ODD = [(1, 1, 1), (2, 1, 5), (3, 9, 13), (2, 100, 37), (1, 37, 100), (4, 1030, 7), (1, 257, 511), (5, 66, 130)]
+
+
+@pytest.mark.parametrize("shape", ODD)
+def test_dims_not_multiple_of_8(shape):
+    # zero-padded to multiples of 8 internally; the result is NS of the
+    # caller's matrix (zero rows / columns add only zero singular values)
+    dev = device()
+    x = gaussian(shape, 800 + sum(shape), torch.float32)
+    ref = newton_schulz_batched(x.double().numpy())
+    y32 = ns.orthogonalize(x.to(dev))
+    yb = ns.orthogonalize(x.to(torch.bfloat16).to(dev))
+    torch.cuda.synchronize()
+    assert y32.shape == x.shape and yb.shape == x.shape
+    assert rel_err(to64(y32), ref).max() <= 1e-4
+    # bf16: 1e-2, or 1.25 x the CPU rounding model's floor where a tiny slice
+    # puts that floor above 1e-2 (slice 0 of 3x9x13: 1.12e-2)
+    floor = np.array([rel_err(ns_bf16_model(x[i].to(torch.bfloat16).float().numpy(), placement="diag"),
+                              ref[i])[0] for i in range(shape[0])])
+    e = rel_err(to64(yb), ref)
+    report({"case": f"odd_bf16_{shape}", "errs": e.tolist(), "model_floor": floor.tolist()})
+    assert np.all(e <= np.maximum(1e-2, 1.25 * floor)), (e, floor)
+    assert "zero-padded" in ns.ns_query_last_config()
+
+
+@pytest.mark.parametrize("steps", [0, 1, 2, 3])
+def test_dims_not_multiple_of_8_in_place_and_steps(steps):
+    dev = device()
+    x = gaussian((3, 45, 70), 900 + steps, torch.float32).to(dev)
+    want = ns.orthogonalize(x.clone(), steps=steps)
+    ns.orthogonalize(x, steps=steps, out=x)
+    torch.cuda.synchronize()
+    assert torch.equal(x, want)
+    ref = newton_schulz_batched(gaussian((3, 45, 70), 900 + steps, torch.float32).double().numpy(), steps=steps)
+    assert rel_err(to64(x), ref).max() <= 1e-4
 
 
 def test_config_query_names_the_kernels():
