@@ -104,6 +104,46 @@ int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows,
 /* Bytes of library workspace one ns_orthogonalize call of this shape needs. */
 size_t ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int dtype);
 
+/*
+ * ns_orthogonalize_grouped - the same method on several stacks of different
+ * shapes in one call (param-decomp PR #978, "What": same-shape leaves are
+ * batched into one NS; here leaves of different shapes share the launches
+ * too, and prime-rl PR #3873, "Summary" item 2: each slice on its own).
+ *
+ *   n_groups  number of stacks, 0..NS_MAX_GROUPS (0 enqueues nothing).
+ *   in, out   HOST arrays of n_groups DEVICE pointers; stack g is
+ *             [batch[g], rows[g], cols[g]] row-major at in[g], result at
+ *             out[g], with ns_orthogonalize's rules for each pair
+ *             (out[g] == in[g] allowed, any other overlap is an error).
+ *             No out[g] may overlap another stack's in or out.
+ *   batch, rows, cols
+ *             HOST arrays of n_groups sizes, each checked as in
+ *             ns_orthogonalize (batch[g] == 0: stack g is skipped and
+ *             its pointers are not read, so they may be NULL).
+ *   dtype, ns_steps, a, b, c, stream
+ *             as in ns_orthogonalize, shared by every stack.
+ *
+ * The host arrays are read during the call only.  Each step runs at most
+ * five launches whatever the number of stacks (Gram of the wide stacks,
+ * Gram of the tall ones, one poly over all, update of the wide, update of
+ * the tall; each split per 16 stacks), so many small leaves fill the GPU
+ * together.  Every slice's result is bitwise the one ns_orthogonalize gives
+ * for it.  ns_steps == 0 runs the stacks one after another.  Errors in any
+ * stack are reported before anything is enqueued, with the stack's index in
+ * ns_last_error().
+ */
+#define NS_MAX_GROUPS 4096
+int ns_orthogonalize_grouped(int n_groups, const void* const* in, void* const* out,
+                             const int64_t* batch, const int64_t* rows,
+                             const int64_t* cols, int dtype, int ns_steps,
+                             float a, float b, float c, void* stream);
+
+/* Bytes of library workspace one ns_orthogonalize_grouped call needs (0 for
+ * invalid arguments). */
+size_t ns_workspace_bytes_grouped(int n_groups, const int64_t* batch,
+                                  const int64_t* rows, const int64_t* cols,
+                                  int dtype);
+
 /* Free every cached workspace (all devices and streams).  Synchronises each
  * device that held one.  Returns NS_OK or NS_ERR_HIP. */
 int ns_release_workspace(void);

@@ -25,9 +25,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libns_hip.s
 
 # exported symbols and their C signatures (include/ns_hip.h)
 _i64, _int, _flt, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+_pvp, _pi64 = ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int64)
+NS_MAX_GROUPS = 4096
 SIGNATURES = {
     "ns_orthogonalize": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _flt, _flt, _flt, _vp]),
     "ns_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
+    "ns_orthogonalize_grouped": (_int, [_int, _pvp, _pvp, _pi64, _pi64, _pi64, _int, _int, _flt, _flt, _flt, _vp]),
+    "ns_workspace_bytes_grouped": (_sz, [_int, _pi64, _pi64, _pi64, _int]),
     "ns_release_workspace": (_int, []),
     "ns_status_string": (ctypes.c_char_p, [_int]),
     "ns_last_error": (ctypes.c_char_p, []),
@@ -127,6 +131,56 @@ def orthogonalize(x, steps=DEFAULT_STEPS, coeffs=DEFAULT_COEFFS, out=None):
     """Convenience form: orthogonalize(x, steps, (a, b, c))."""
     a, b, c = coeffs
     return ns_orthogonalize(x, out=out, ns_steps=steps, a=a, b=b, c=c)
+
+
+def _arrays(shapes):
+    n = len(shapes)
+    return ((ctypes.c_int64 * n)(*[s[0] for s in shapes]), (ctypes.c_int64 * n)(*[s[1] for s in shapes]),
+            (ctypes.c_int64 * n)(*[s[2] for s in shapes]))
+
+
+def ns_orthogonalize_grouped(xs, outs=None, ns_steps=DEFAULT_STEPS, a=DEFAULT_COEFFS[0], b=DEFAULT_COEFFS[1],
+                             c=DEFAULT_COEFFS[2]):
+    """Newton–Schulz of every slice of several stacks of different shapes in one
+    call (shared launches); xs is a list of tensors of one dtype on one device.
+    Returns the list of outputs."""
+    import torch
+    xs = list(xs)
+    if not xs:
+        return []
+    if outs is None:
+        outs = [torch.empty_like(x) for x in xs]
+    outs = list(outs)
+    if len(outs) != len(xs):
+        raise ValueError("outs must have one tensor per input")
+    dev, dt = xs[0].device, xs[0].dtype
+    for i, (x, o) in enumerate(zip(xs, outs)):
+        _need_gpu_tensor(x, f"xs[{i}]")
+        _need_gpu_tensor(o, f"outs[{i}]")
+        if x.device != dev or o.device != dev or x.dtype != dt or o.dtype != dt:
+            raise ValueError("every tensor must share the first input's device and dtype")
+        if o.shape != x.shape:
+            raise ValueError(f"outs[{i}] must match xs[{i}] in shape")
+    n = len(xs)
+    bt, rt, ct = _arrays([_brc(x) for x in xs])
+    pin = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+    pout = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+    with torch.cuda.device(dev):
+        _check(lib().ns_orthogonalize_grouped(n, pin, pout, bt, rt, ct, _dtype_code(xs[0]), int(ns_steps),
+                                              float(a), float(b), float(c), _stream(xs[0])))
+    return outs
+
+
+def orthogonalize_grouped(xs, steps=DEFAULT_STEPS, coeffs=DEFAULT_COEFFS, outs=None):
+    """Convenience form: orthogonalize_grouped([x0, x1, ...], steps, (a, b, c))."""
+    a, b, c = coeffs
+    return ns_orthogonalize_grouped(xs, outs=outs, ns_steps=steps, a=a, b=b, c=c)
+
+
+def ns_workspace_bytes_grouped(shapes, dtype_code):
+    """Workspace bytes of a grouped call over stacks of the given (batch, rows, cols)."""
+    bt, rt, ct = _arrays(shapes)
+    return int(lib().ns_workspace_bytes_grouped(len(shapes), bt, rt, ct, dtype_code))
 
 
 def ns_workspace_bytes(batch, rows, cols, dtype_code):

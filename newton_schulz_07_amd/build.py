@@ -22,6 +22,10 @@ HIP_FLAGS = [
     "-fPIC",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # multiply-adds fuse only where the source writes them as one expression
+    # or fmaf, never by the backend's choice, so every kernel instance of the
+    # same arithmetic rounds the same way
+    "-ffp-contract=on",
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,
 ]

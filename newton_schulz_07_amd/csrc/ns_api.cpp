@@ -239,6 +239,93 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
+// ------------------------------------------------------- grouped calls
+
+// One stack of a grouped call: its plan, its part of the shared workspace
+// and its buffers (in / out are the zero-padded workspace copies when the
+// plan is padded).
+struct Group {
+  Plan p;
+  size_t ws_off;
+  const void* uin;
+  void* uout;
+  const void* in;
+  void* out;
+  bool copy_in;
+  void *xtmp, *oa, *oc;
+  float *da, *dc, *part;
+};
+
+// Plans of the non-empty stacks and the workspace they need together.
+size_t plan_groups(int n, const int64_t* batch, const int64_t* rows, const int64_t* cols, int dtype,
+                   std::vector<Group>* gs) {
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    if (batch[i] == 0) continue;
+    Group g{};
+    g.p = make_plan(batch[i], rows[i], cols[i], dtype);
+    g.ws_off = off;
+    off += ns::ws_align(g.p.total);
+    if (gs) gs->push_back(g);
+  }
+  return off;
+}
+
+int check_grouped(int n, const void* const* in, void* const* out, const int64_t* batch, const int64_t* rows,
+                  const int64_t* cols, int dtype) {
+  if (n < 0 || n > NS_MAX_GROUPS)
+    return fail(NS_ERR_INVALID_ARG, "n_groups must be in [0, " + std::to_string(NS_MAX_GROUPS) + "]");
+  if (n == 0) return NS_OK;
+  if (!batch || !rows || !cols) return fail(NS_ERR_INVALID_ARG, "batch, rows and cols arrays must not be NULL");
+  if (int s = check_dtype(dtype)) return s;
+  for (int i = 0; i < n; ++i)
+    if (int s = check_shape(batch[i], rows[i], cols[i], true))
+      return fail(s, "stack " + std::to_string(i) + ": " + t_err);
+  if (in == nullptr && out == nullptr) return NS_OK;  // sizes only (workspace query)
+  if (!in || !out) return fail(NS_ERR_INVALID_ARG, "in and out arrays must not be NULL");
+  std::vector<size_t> bytes(n, 0);
+  for (int i = 0; i < n; ++i) {
+    if (batch[i] == 0) continue;  // skipped stack: its pointers are never used
+    const std::string who = "stack " + std::to_string(i) + ": ";
+    if (int s = check_ptr(in[i], "in")) return fail(s, who + t_err);
+    if (int s = check_ptr(out[i], "out")) return fail(s, who + t_err);
+    bytes[i] = (size_t)batch[i] * rows[i] * cols[i] * esize(dtype);
+    if (in[i] != out[i] && overlaps(in[i], bytes[i], out[i], bytes[i]))
+      return fail(NS_ERR_INVALID_ARG, who + "out overlaps in without being the same pointer");
+  }
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j) {
+      if (i == j || bytes[i] == 0 || bytes[j] == 0) continue;
+      if (overlaps(out[i], bytes[i], in[j], bytes[j]) || (i < j && overlaps(out[i], bytes[i], out[j], bytes[j])))
+        return fail(NS_ERR_INVALID_ARG,
+                    "out of stack " + std::to_string(i) + " overlaps the buffers of stack " + std::to_string(j));
+    }
+  return NS_OK;
+}
+
+void record_config_grouped(const std::vector<Group>& gs, const ns::TileChoice& tc, int steps, int launches[3]) {
+  const int dtype = gs[0].p.dtype;
+  int nt = 0;
+  for (const Group& g : gs) nt += g.p.tall;
+  const ns::TileCfg tw = ns::tile_cfg(dtype, true, tc.gram_wide), tt = ns::tile_cfg(dtype, true, tc.gram_tall);
+  const ns::TileCfg tp = ns::tile_cfg(dtype, true, tc.poly), tr = ns::tile_cfg(dtype, false);
+  char buf[512];
+  std::snprintf(buf, sizeof(buf),
+                "grouped: %d stacks (%d wide, %d tall) dtype=%s steps=%d | norm: sumsq, one launch, 1/||x|| folded "
+                "into step 1 | launches per step: gram %d, poly %d, update %d | gram wide: lower-tri tile=%dx%d | "
+                "gram tall: lower-tri tile=%dx%d | poly: lower-tri tile=%dx%d%s | update: tile=%dx%d",
+                (int)gs.size(), (int)gs.size() - nt, nt, dtype == NS_DTYPE_BF16 ? "bf16" : "fp32", steps,
+                launches[0], launches[1], launches[2], tw.bm, tw.bn, tt.bm, tt.bn, tp.bm, tp.bn,
+                tc.lower_only ? " (A read as its lower block triangle)" : "", tr.bm, tr.bn);
+  t_cfg = buf;
+  t_cfg += " | stacks:";
+  for (size_t i = 0; i < gs.size() && i < 64; ++i) {
+    const Plan& p = gs[i].p;
+    t_cfg += " " + std::to_string(p.batch) + "x" + std::to_string(p.urows) + "x" + std::to_string(p.ucols);
+  }
+  if (gs.size() > 64) t_cfg += " ...";
+}
+
 }  // namespace
 
 // =================================================================== C ABI
@@ -305,6 +392,144 @@ int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows, int
   }
   record_config(p, ns_steps);
   return NS_OK;
+}
+
+int ns_orthogonalize_grouped(int n_groups, const void* const* in, void* const* out, const int64_t* batch,
+                             const int64_t* rows, const int64_t* cols, int dtype, int ns_steps, float a, float b,
+                             float c, void* stream) {
+  t_err.clear();
+  if (in == nullptr || out == nullptr) {
+    if (n_groups > 0) return fail(NS_ERR_INVALID_ARG, "in and out arrays must not be NULL");
+  }
+  if (int s = check_grouped(n_groups, in, out, batch, rows, cols, dtype)) return s;
+  if (ns_steps < 0) return fail(NS_ERR_INVALID_ARG, "ns_steps must be >= 0");
+  std::vector<Group> gs;
+  const size_t total = plan_groups(n_groups, batch, rows, cols, dtype, &gs);
+  if (gs.empty()) return NS_OK;
+  if (int s = check_arch()) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (ns_steps == 0) {  // normalisation only: the stacks one after another
+    for (int i = 0; i < n_groups; ++i)
+      if (batch[i] > 0)
+        if (int s = ns_orthogonalize(in[i], out[i], batch[i], rows[i], cols[i], dtype, 0, a, b, c, stream))
+          return fail(s, "stack " + std::to_string(i) + ": " + t_err);
+    t_cfg = "grouped: " + std::to_string(gs.size()) + " stacks, ns_steps=0: normalised one by one";
+    return NS_OK;
+  }
+  char* ws = nullptr;
+  if (int s = get_workspace(st, total, &ws)) return s;
+  {
+    int k = 0;
+    for (int i = 0; i < n_groups; ++i) {
+      if (batch[i] == 0) continue;
+      Group& g = gs[k++];
+      char* w = ws + g.ws_off;
+      g.uin = in[i];
+      g.uout = out[i];
+      g.in = in[i];
+      g.out = out[i];
+      g.xtmp = w + g.p.off_xtmp;
+      g.oa = w + g.p.off_oa;
+      g.oc = w + g.p.off_oc;
+      g.da = reinterpret_cast<float*>(w + g.p.off_da);
+      g.dc = reinterpret_cast<float*>(w + g.p.off_dc);
+      g.part = reinterpret_cast<float*>(w + g.p.off_part);
+    }
+  }
+  const int n = (int)gs.size();
+  std::vector<Plan> plans;
+  for (const Group& g : gs) plans.push_back(g.p);
+  const ns::TileChoice tc = ns::choose_tiles(plans.data(), n);
+
+  // odd shapes run on zero-padded copies; in-place calls with an odd step
+  // count start from a copy of the input (as in ns_orthogonalize)
+  for (Group& g : gs) {
+    if (g.p.padded) {
+      const ns::PadArgs pa = ns::pad_args(g.p, g.uin, ws + g.ws_off + g.p.off_pin, true);
+      if (int s = check_hip(ns::launch_pad(dtype, pa, st), "pad launch")) return s;
+      g.in = ws + g.ws_off + g.p.off_pin;
+      g.out = ws + g.ws_off + g.p.off_pout;
+    }
+    g.copy_in = ns::input_copy_needed(ns_steps, g.in == g.out);
+  }
+  // one sum-of-squares launch over every stack (the norm is folded into step 1)
+  {
+    std::vector<NormArgs> na;
+    std::vector<int> nb;
+    for (const Group& g : gs) {
+      na.push_back(ns::norm_args(g.p, g.in, nullptr, nullptr, g.part));
+      nb.push_back((int)g.p.batch);
+    }
+    if (int s = check_hip(timed_launch(NS_KIND_SUMSQ, st,
+                                       [&] { return ns::launch_sumsq_grouped(dtype, na.data(), nb.data(), n, st); }),
+                          "sum-of-squares launch"))
+      return s;
+  }
+  for (const Group& g : gs)
+    if (g.copy_in) {
+      const size_t pb = (size_t)g.p.batch * g.p.rows * g.p.cols * esize(dtype);
+      if (int s = check_hip(hipMemcpyAsync(g.xtmp, g.in, pb, hipMemcpyDeviceToDevice, st), "input copy")) return s;
+    }
+  auto buf = [&](const Group& g, int s) -> const void* {
+    if (s == 0) return g.copy_in ? g.xtmp : g.in;
+    return ns::iterate_in_out(ns_steps, s) ? g.out : g.xtmp;
+  };
+  auto wbuf = [&](const Group& g, int s) -> void* { return ns::iterate_in_out(ns_steps, s) ? g.out : g.xtmp; };
+  int launches[3] = {0, 0, 0};
+  for (int s = 1; s <= ns_steps; ++s) {
+    const bool first = s == 1;
+    for (int o = 0; o < 2; ++o) {  // Gram: wide stacks, then tall ones
+      std::vector<GemmArgs> ga;
+      ns::StageKind k{};
+      for (const Group& g : gs)
+        if (g.p.tall == (o == 1))
+          ga.push_back(ns::gram_args(g.p, tc, buf(g, s - 1), g.oa, g.da, &k, first ? g.part : nullptr,
+                                     !tc.lower_only));
+      if (ga.empty()) continue;
+      launches[0] += s == 1;
+      if (int e = check_hip(timed_launch(NS_KIND_GRAM, st,
+                                         [&] { return ns::launch_gemm_grouped(dtype, k, ga.data(), (int)ga.size(), st); }),
+                            "gram launch"))
+        return e;
+    }
+    {
+      std::vector<GemmArgs> ga;
+      ns::StageKind k{};
+      for (const Group& g : gs) ga.push_back(ns::poly_args(g.p, tc, g.oa, g.da, g.oc, g.dc, a, b, c, &k));
+      launches[1] += s == 1;
+      if (int e = check_hip(timed_launch(NS_KIND_POLY, st,
+                                         [&] { return ns::launch_gemm_grouped(dtype, k, ga.data(), n, st); }),
+                            "poly launch"))
+        return e;
+    }
+    for (int o = 0; o < 2; ++o) {  // update: wide stacks, then tall ones
+      std::vector<GemmArgs> ga;
+      ns::StageKind k{};
+      for (const Group& g : gs)
+        if (g.p.tall == (o == 1))
+          ga.push_back(ns::update_args(g.p, buf(g, s - 1), g.oc, g.dc, wbuf(g, s), &k, first ? g.part : nullptr));
+      if (ga.empty()) continue;
+      launches[2] += s == 1;
+      if (int e = check_hip(timed_launch(NS_KIND_UPDATE, st,
+                                         [&] { return ns::launch_gemm_grouped(dtype, k, ga.data(), (int)ga.size(), st); }),
+                            "update launch"))
+        return e;
+    }
+  }
+  for (const Group& g : gs)
+    if (g.p.padded) {
+      const ns::PadArgs pa = ns::pad_args(g.p, g.out, g.uout, false);
+      if (int s = check_hip(ns::launch_pad(dtype, pa, st), "unpad launch")) return s;
+    }
+  record_config_grouped(gs, tc, ns_steps, launches);
+  return NS_OK;
+}
+
+size_t ns_workspace_bytes_grouped(int n_groups, const int64_t* batch, const int64_t* rows, const int64_t* cols,
+                                  int dtype) {
+  if (check_grouped(n_groups, nullptr, nullptr, batch, rows, cols, dtype) != NS_OK) return 0;
+  if (n_groups == 0) return 0;
+  return plan_groups(n_groups, batch, rows, cols, dtype, nullptr);
 }
 
 size_t ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int dtype) {

@@ -175,8 +175,11 @@ void replay_frag_reads(const TileCfg& t, int es, bool nat, int rows_region, int 
   (void)wave_rows;
 }
 
-// Replays one launch of gemm_kernel (grid = tiles_per_slice * batch).
-void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool coverage, const char* what) {
+// Replays one launch of gemm_kernel (grid = tiles_per_slice * batch), or,
+// with `lins`, the workgroups of a grouped launch that fall on this group
+// (their logical tile ids within the group).
+void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool coverage, const char* what,
+                 const std::vector<int>* lins = nullptr) {
   const int mode = kind.mode;
   const bool tri = mode_is_tri(mode);
   const TileCfg t = tile_cfg(dtype, tri, kind.tri_cls);
@@ -212,10 +215,16 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
     if (kind.q_sym) replay_frag_reads(t, es, true, t.bn, WTN, SN, wn * WTN, what);
   }
 
-  for (int w = 0; w < G; ++w) {
-    const int lin = xcd_remap(w, G);
+  std::vector<int> order;
+  if (lins) {
+    order = *lins;
+    if ((long long)order.size() != G) fail(std::string(what) + ": grouped launch gives a group the wrong tile count");
+  } else {
+    for (int w = 0; w < G; ++w) order.push_back(xcd_remap(w, G));
+  }
+  for (int lin : order) {
     if (lin < 0 || lin >= G || seen[lin]) {
-      fail(std::string(what) + ": xcd_remap is not a bijection");
+      fail(std::string(what) + ": tile ids are not a bijection");
       continue;
     }
     seen[lin] = 1;
@@ -432,6 +441,38 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
   }
 }
 
+// A launch over several groups (mirrors launch_mode / gemm_kernel with NG >
+// 1): split as the launcher splits, map every workgroup of each launch to
+// its group and tile id, then replay each group on exactly those ids.
+void replay_gemm_grouped(const std::vector<GemmArgs>& gs, const StageKind& kind, int dtype, bool coverage,
+                         const char* what) {
+  if (gs.size() == 1) {
+    replay_gemm(gs[0], kind, dtype, coverage, what);
+    return;
+  }
+  for (int g0 = 0; g0 < (int)gs.size();) {
+    int start[kMaxLaunchGroups];
+    long long total = 0;
+    const int k = launch_chunk(
+        (int)gs.size() - g0, [&](int i) { return (long long)gs[g0 + i].tiles_per_slice * gs[g0 + i].batch; },
+        start, &total);
+    if (k < 1) {
+      fail(std::string(what) + ": empty launch");
+      return;
+    }
+    std::vector<std::vector<int>> lins(k);
+    for (long long w = 0; w < total; ++w) {
+      const int lin_all = xcd_remap((int)w, (int)total);
+      const int grp = launch_group(lin_all, start, k);
+      if (lin_all < start[grp] || (grp + 1 < k && lin_all >= start[grp + 1]))
+        fail(std::string(what) + ": workgroup mapped to the wrong group");
+      lins[grp].push_back(lin_all - start[grp]);
+    }
+    for (int i = 0; i < k; ++i) replay_gemm(gs[g0 + i], kind, dtype, coverage, what, &lins[i]);
+    g0 += k;
+  }
+}
+
 void replay_norm(const NormArgs& g, int batch, bool scale, const char* what) {
   const int NT = 256;
   for (int slice = 0; slice < batch; ++slice)
@@ -455,6 +496,35 @@ void replay_norm(const NormArgs& g, int batch, bool scale, const char* what) {
         access(g.partials, ((long long)slice * g.chunks + chunk) * 4, 4, what);
       }
     }
+}
+
+// The grouped sum-of-squares launch (mirrors sumsq_grouped_kernel): every
+// block maps to a distinct (group, slice, chunk), and each group's blocks
+// are then the plain launch's.
+void replay_norm_grouped(const std::vector<NormArgs>& gs, const std::vector<int>& batch, const char* what) {
+  for (int g0 = 0; g0 < (int)gs.size();) {
+    int start[kMaxLaunchGroups];
+    long long total = 0;
+    const int k = launch_chunk(
+        (int)gs.size() - g0, [&](int i) { return (long long)gs[g0 + i].chunks * batch[g0 + i]; }, start, &total);
+    std::vector<std::vector<uint8_t>> seen(k);
+    for (int i = 0; i < k; ++i) seen[i].assign((size_t)gs[g0 + i].chunks * batch[g0 + i], 0);
+    for (long long b = 0; b < total; ++b) {
+      const int grp = launch_group((int)b, start, k);
+      const long long local = b - start[grp];
+      const NormArgs& a = gs[g0 + grp];
+      const long long slice = local / a.chunks, chunk = local % a.chunks;
+      if (slice >= batch[g0 + grp] || local >= (long long)seen[grp].size() || seen[grp][local]++)
+        fail(std::string(what) + ": grouped norm block maps outside its group or twice");
+      (void)chunk;
+    }
+    for (int i = 0; i < k; ++i) {
+      for (uint8_t v : seen[i])
+        if (v != 1) fail(std::string(what) + ": grouped norm block not covered once");
+      replay_norm(gs[g0 + i], batch[g0 + i], false, what);
+    }
+    g0 += k;
+  }
 }
 
 // Pad or unpad (mirrors pad_kernel): destination element e of every slice,
@@ -533,11 +603,125 @@ void replay_call(int dtype, long long batch, long long urows, long long ucols, i
   if (p.padded) replay_pad(pad_args(p, out, uout, false), es, "unpad");
 }
 
+// Replays one ns_orthogonalize_grouped call as the driver sequences it.
+struct Shape {
+  long long batch, rows, cols;
+};
+void replay_grouped_call(int dtype, int steps, const std::vector<Shape>& shapes, bool alias) {
+  if (steps == 0) {  // the driver normalises the stacks one by one
+    for (const Shape& sh : shapes)
+      if (sh.batch > 0) replay_call(dtype, sh.batch, sh.rows, sh.cols, 0, alias);
+    return;
+  }
+  g_bufs.clear();
+  g_written.clear();
+  struct G {
+    Plan p;
+    void *uin, *uout, *in, *out, *xtmp, *oa, *oc;
+    float *da, *dc, *part;
+    bool copy_in;
+  };
+  std::vector<G> gs;
+  const int es = (int)elem_size(dtype);
+  for (size_t i = 0; i < shapes.size(); ++i) {
+    const Shape& sh = shapes[i];
+    if (sh.batch == 0) continue;
+    G g{};
+    g.p = make_plan(sh.batch, sh.rows, sh.cols, dtype);
+    const Plan& p = g.p;
+    auto at = [&](int k) { return (uintptr_t(16 * (i + 1) + k)) << 40; };
+    const std::string id = "[" + std::to_string(i) + "]";
+    const size_t ubytes = (size_t)sh.batch * sh.rows * sh.cols * es, xbytes = (size_t)p.batch * p.rows * p.cols * es;
+    const size_t mm = (size_t)p.batch * p.m * p.m * es;
+    g.uin = reg(at(1), "in" + id, ubytes);
+    g.uout = alias ? g.uin : reg(at(2), "out" + id, ubytes);
+    g.in = g.uin;
+    g.out = g.uout;
+    if (p.padded) {
+      g.in = reg(at(9), "padded in" + id, xbytes);
+      g.out = reg(at(10), "padded out" + id, xbytes);
+      replay_pad(pad_args(p, g.uin, g.in, true), es, "pad");
+    }
+    g.xtmp = reg(at(3), "xtmp" + id, xbytes);
+    g.oa = reg(at(4), "oa" + id, mm);
+    g.oc = reg(at(5), "oc" + id, mm);
+    g.da = (float*)reg(at(6), "da" + id, (size_t)p.batch * p.m * 4);
+    g.dc = (float*)reg(at(7), "dc" + id, (size_t)p.batch * p.m * 4);
+    g.part = (float*)reg(at(8), "partials" + id, (size_t)p.batch * p.norm_chunks * 4);
+    g.copy_in = input_copy_needed(steps, g.in == g.out);
+    gs.push_back(g);
+  }
+  if (gs.empty()) return;
+  std::vector<Plan> plans;
+  for (const G& g : gs) plans.push_back(g.p);
+  const TileChoice tc = choose_tiles(plans.data(), (int)plans.size());
+  {
+    std::vector<NormArgs> na;
+    std::vector<int> nb;
+    for (const G& g : gs) {
+      na.push_back(norm_args(g.p, g.in, nullptr, nullptr, g.part));
+      nb.push_back((int)g.p.batch);
+    }
+    replay_norm_grouped(na, nb, "grouped sumsq");
+  }
+  auto wbuf = [&](const G& g, int s) -> void* { return iterate_in_out(steps, s) ? g.out : g.xtmp; };
+  auto buf = [&](const G& g, int s) -> void* { return s == 0 ? (g.copy_in ? g.xtmp : g.in) : wbuf(g, s); };
+  long long elems = 0;
+  for (const G& g : gs) elems += g.p.batch * std::max<long long>(g.p.m * g.p.m, g.p.rows * g.p.cols);
+  const bool cov = elems <= 80LL * 1000 * 1000;
+  for (int s = 1; s <= steps; ++s) {
+    if (s != 1 && s != steps && s != 2) continue;
+    StageKind kind;
+    for (int o = 0; o < 2; ++o) {
+      std::vector<GemmArgs> ga;
+      for (const G& g : gs)
+        if (g.p.tall == (o == 1))
+          ga.push_back(gram_args(g.p, tc, buf(g, s - 1), g.oa, g.da, &kind, s == 1 ? g.part : nullptr,
+                                 !tc.lower_only));
+      if (!ga.empty()) replay_gemm_grouped(ga, kind, dtype, cov, "grouped gram");
+    }
+    {
+      std::vector<GemmArgs> ga;
+      for (const G& g : gs) ga.push_back(poly_args(g.p, tc, g.oa, g.da, g.oc, g.dc, 3.4445f, -4.775f, 2.0315f, &kind));
+      replay_gemm_grouped(ga, kind, dtype, cov, "grouped poly");
+    }
+    for (int o = 0; o < 2; ++o) {
+      std::vector<GemmArgs> ga;
+      for (const G& g : gs)
+        if (g.p.tall == (o == 1)) {
+          if (buf(g, s - 1) == wbuf(g, s)) fail("update reads the buffer it writes");
+          ga.push_back(update_args(g.p, buf(g, s - 1), g.oc, g.dc, wbuf(g, s), &kind, s == 1 ? g.part : nullptr));
+        }
+      if (!ga.empty()) replay_gemm_grouped(ga, kind, dtype, cov, "grouped update");
+    }
+  }
+  for (const G& g : gs) {
+    if (steps >= 1 && wbuf(g, steps) != g.out) fail("the last step does not write the result buffer");
+    if (g.p.padded) replay_pad(pad_args(g.p, g.out, g.uout, false), es, "unpad");
+  }
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
+  // grouped call: --group dtype steps b r c [b r c ...]
+  if (argc >= 7 && std::string(argv[1]) == "--group" && (argc - 4) % 3 == 0) {
+    const int dtype = std::atoi(argv[2]), steps = std::atoi(argv[3]);
+    std::vector<Shape> shapes;
+    for (int a = 4; a + 2 < argc; a += 3)
+      shapes.push_back(Shape{std::atoll(argv[a]), std::atoll(argv[a + 1]), std::atoll(argv[a + 2])});
+    for (int alias = 0; alias < 2; ++alias) {
+      const int before = g_fail;
+      replay_grouped_call(dtype, steps, shapes, alias != 0);
+      std::printf("%s grouped dtype=%d steps=%d stacks=%d alias=%d\n", g_fail == before ? "OK  " : "FAIL", dtype,
+                  steps, (int)shapes.size(), alias);
+    }
+    std::printf("checks=%lld violations=%d\n", g_checks, g_fail);
+    return g_fail == 0 ? 0 : 1;
+  }
   if (argc < 6 || (argc - 1) % 5 != 0) {
-    std::fprintf(stderr, "usage: %s dtype batch rows cols steps [...]\n", argv[0]);
+    std::fprintf(stderr, "usage: %s dtype batch rows cols steps [...]\n       %s --group dtype steps b r c [...]\n",
+                 argv[0], argv[0]);
     return 2;
   }
   for (int a = 1; a + 4 < argc; a += 5) {

@@ -175,8 +175,10 @@ __device__ __forceinline__ int nat_lane_byte(int rb, int h, int lane, int rc, fl
 
 // OCC workgroups of WM x WN waves per CU: at least OCC WM WN / 4 waves on each
 // of the CU's four SIMDs (HIP's second launch bound), which caps the VGPRs.
-template <typename T, int BM, int BN, int WM, int WN, int CPR, int ST, int OCC, int MODE, int PL, int QL>
-__global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_kernel(const GemmArgs g) {
+// NG > 1: the launch covers up to NG groups of slices of different shapes
+// (GemmLaunch); the workgroup's group is found from its logical tile id.
+template <typename T, int BM, int BN, int WM, int WN, int CPR, int ST, int OCC, int MODE, int PL, int QL, int NG>
+__global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_kernel(const GemmLaunch<NG> L) {
   // operand layouts (OperandLayout): which read paths each operand needs
   constexpr bool PNAT = PL == LAY_NAT, QNAT = QL == LAY_NAT;
   constexpr bool P_KC = PL != LAY_NAT, P_NT = PL != LAY_KCONT;  // K-contiguous / natural reads of P
@@ -205,7 +207,10 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int lin_all = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = NG > 1 ? launch_group(lin_all, L.start, L.n) : 0;
+  const GemmArgs& g = L.g[grp];
+  const int lin = NG > 1 ? lin_all - L.start[grp] : lin_all;
   const int slice = lin / g.tiles_per_slice;
   const int q = lin - slice * g.tiles_per_slice;
   int ti, tj;
@@ -413,7 +418,7 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
             float x[4];
             Quad<T>::unpack(*reinterpret_cast<const QRaw*>(reinterpret_cast<const T*>(Qs + pos) + jl % EPC), x);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[a][b][4 * rg + e] += drow[a] * x[e];
+            for (int e = 0; e < 4; ++e) acc[a][b][4 * rg + e] = fmaf(drow[a], x[e], acc[a][b][4 * rg + e]);
           }
       }
     } else if (MODE == MODE_UPD_COL || MODE == MODE_POLY) {
@@ -443,10 +448,10 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
             } else {
               float x[4];
               Quad<T>::unpack(raw, x);
-              acc[a][b][4 * rg + 0] += dj.x * x[0];
-              acc[a][b][4 * rg + 1] += dj.y * x[1];
-              acc[a][b][4 * rg + 2] += dj.z * x[2];
-              acc[a][b][4 * rg + 3] += dj.w * x[3];
+              acc[a][b][4 * rg + 0] = fmaf(dj.x, x[0], acc[a][b][4 * rg + 0]);
+              acc[a][b][4 * rg + 1] = fmaf(dj.y, x[1], acc[a][b][4 * rg + 1]);
+              acc[a][b][4 * rg + 2] = fmaf(dj.z, x[2], acc[a][b][4 * rg + 2]);
+              acc[a][b][4 * rg + 3] = fmaf(dj.w, x[3], acc[a][b][4 * rg + 3]);
             }
           }
         }
@@ -552,9 +557,10 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
           const float di = din[i];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            w[e] = cb * o[e] + cc * (v[e] + (di + dje[e]) * o[e]);
+            // b O_A + c (O_A O_A + (d_i + d_j) O_A); diagonal: a + b d_i + c ((O_A O_A)_ii + d_i^2)
+            w[e] = fmaf(cb, o[e], cc * fmaf(di + dje[e], o[e], v[e]));
             if (i == j + e) {
-              dout[i] = g.ca + cb * di + cc * (v[e] + di * di);
+              dout[i] = fmaf(cc, fmaf(di, di, v[e]), fmaf(cb, di, g.ca));
               w[e] = 0.0f;
             }
           }
@@ -668,9 +674,8 @@ constexpr int kNormThreads = 256;
 
 // Pass 1: partial sums of squares, one per (chunk, slice) block, fixed order.
 template <typename T>
-__global__ __launch_bounds__(kNormThreads) void sumsq_kernel(const NormArgs g) {
+__device__ __forceinline__ void sumsq_block(const NormArgs& g, int slice, int chunk) {
   __shared__ float red[kNormThreads / 64];
-  const int slice = blockIdx.y, chunk = blockIdx.x;
   const uint4* xv = reinterpret_cast<const uint4*>(g.x) + (size_t)slice * g.slice_vecs;
   const long long v0 = (long long)chunk * g.chunk_vecs;
   const long long v1 = (v0 + g.chunk_vecs < g.slice_vecs) ? v0 + g.chunk_vecs : g.slice_vecs;
@@ -685,6 +690,19 @@ __global__ __launch_bounds__(kNormThreads) void sumsq_kernel(const NormArgs g) {
     for (int w = 0; w < kNormThreads / 64; ++w) t += red[w];
     g.partials[(size_t)slice * g.chunks + chunk] = t;
   }
+}
+template <typename T>
+__global__ __launch_bounds__(kNormThreads) void sumsq_kernel(const NormArgs g) {
+  sumsq_block<T>(g, blockIdx.y, blockIdx.x);
+}
+// several stacks in one launch (NormLaunch): a 1-D grid of blocks
+template <typename T>
+__global__ __launch_bounds__(kNormThreads) void sumsq_grouped_kernel(const NormLaunch<kMaxLaunchGroups> L) {
+  const int b = blockIdx.x;
+  const int grp = launch_group(b, L.start, L.n);
+  const NormArgs& g = L.a[grp];
+  const int local = b - L.start[grp];
+  sumsq_block<T>(g, local / g.chunks, local % g.chunks);
 }
 
 // Pass 2: every block sums its slice's partials (same order in every block),
@@ -737,53 +755,81 @@ __global__ __launch_bounds__(256) void pad_kernel(const PadArgs g) {
 
 // ------------------------------------------------------------- launchers
 
+// A launch over the groups gs[0 .. n): one group is a plain launch (NG = 1);
+// several go out kMaxLaunchGroups at a time, each launch's grid covering the
+// tiles of its groups.
 template <typename T, int MODE, int CLS, int PL, int QL>
-static hipError_t launch_mode(const GemmArgs& g, hipStream_t st) {
+static hipError_t launch_mode(const GemmArgs* gs, int n, hipStream_t st) {
   constexpr TileCfg t = tile_cfg(std::is_same<T, bf16>::value ? 1 : 0, mode_is_tri(MODE), CLS);
-  const int total = g.tiles_per_slice * g.batch;
-  hipLaunchKernelGGL((gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.cpr, t.st, t.occ, MODE, PL, QL>),
-                     dim3(total), dim3(t.wm * t.wn * 64), 0, st, g);
-  return hipGetLastError();
+  const dim3 block(t.wm * t.wn * 64);
+  if (n == 1) {
+    GemmLaunch<1> L{};
+    L.g[0] = gs[0];
+    L.n = 1;
+    hipLaunchKernelGGL((gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.cpr, t.st, t.occ, MODE, PL, QL, 1>),
+                       dim3(gs[0].tiles_per_slice * gs[0].batch), block, 0, st, L);
+    return hipGetLastError();
+  }
+  static_assert(sizeof(GemmLaunch<kMaxLaunchGroups>) <= 4096, "kernel arguments over 4 KiB");
+  for (int g0 = 0; g0 < n;) {
+    GemmLaunch<kMaxLaunchGroups> L{};
+    long long total = 0;
+    const int k = launch_chunk(
+        n - g0, [&](int i) { return (long long)gs[g0 + i].tiles_per_slice * gs[g0 + i].batch; }, L.start, &total);
+    for (int i = 0; i < k; ++i) L.g[i] = gs[g0 + i];
+    L.n = k;
+    hipLaunchKernelGGL((gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.cpr, t.st, t.occ, MODE, PL, QL, kMaxLaunchGroups>),
+                       dim3((unsigned)total), block, 0, st, L);
+    if (hipError_t e = hipGetLastError()) return e;
+    g0 += k;
+  }
+  return hipSuccess;
 }
 
 template <typename T, int MODE, int PL, int QL>
-static hipError_t launch_tri(int cls, const GemmArgs& g, hipStream_t st) {
-  if (!std::is_same<T, bf16>::value) return launch_mode<T, MODE, TRI_NARROW, PL, QL>(g, st);
+static hipError_t launch_tri(int cls, const GemmArgs* gs, int n, hipStream_t st) {
+  if (!std::is_same<T, bf16>::value) return launch_mode<T, MODE, TRI_NARROW, PL, QL>(gs, n, st);
   switch (cls) {
-    case TRI_WIDE: return launch_mode<T, MODE, TRI_WIDE, PL, QL>(g, st);
-    case TRI_BIG: return launch_mode<T, MODE, TRI_BIG, PL, QL>(g, st);
-    default: return launch_mode<T, MODE, TRI_NARROW, PL, QL>(g, st);
+    case TRI_WIDE: return launch_mode<T, MODE, TRI_WIDE, PL, QL>(gs, n, st);
+    case TRI_BIG: return launch_mode<T, MODE, TRI_BIG, PL, QL>(gs, n, st);
+    default: return launch_mode<T, MODE, TRI_NARROW, PL, QL>(gs, n, st);
   }
 }
 
 template <typename T>
-static hipError_t dispatch_mode(const StageKind& k, const GemmArgs& g, hipStream_t st) {
+static hipError_t dispatch_mode(const StageKind& k, const GemmArgs* gs, int n, hipStream_t st) {
   const bool wide = k.tri_cls == TRI_WIDE && std::is_same<T, bf16>::value;
   switch (k.mode) {
     case MODE_GRAM:
-      if (k.p_nat) return launch_tri<T, MODE_GRAM, LAY_NAT, LAY_NAT>(k.tri_cls, g, st);
-      return launch_tri<T, MODE_GRAM, LAY_KCONT, LAY_KCONT>(k.tri_cls, g, st);
+      if (k.p_nat) return launch_tri<T, MODE_GRAM, LAY_NAT, LAY_NAT>(k.tri_cls, gs, n, st);
+      return launch_tri<T, MODE_GRAM, LAY_KCONT, LAY_KCONT>(k.tri_cls, gs, n, st);
     case MODE_POLY:
       // the poly never takes the big tile (see tri_class)
-      // lower-triangle reads of A: bf16, 128 tile (see gram_lower_only)
+      // lower-triangle reads of A: bf16, 128 tile (see TileChoice)
       if (k.p_sym && k.q_sym && std::is_same<T, bf16>::value && !wide)
-        return launch_mode<bf16, MODE_POLY, TRI_NARROW, LAY_SYM, LAY_SYM>(g, st);
+        return launch_mode<bf16, MODE_POLY, TRI_NARROW, LAY_SYM, LAY_SYM>(gs, n, st);
       if (k.p_sym || k.q_sym) return hipErrorInvalidValue;
-      return wide ? launch_mode<T, MODE_POLY, TRI_WIDE, LAY_KCONT, LAY_KCONT>(g, st)
-                  : launch_mode<T, MODE_POLY, TRI_NARROW, LAY_KCONT, LAY_KCONT>(g, st);
+      return wide ? launch_mode<T, MODE_POLY, TRI_WIDE, LAY_KCONT, LAY_KCONT>(gs, n, st)
+                  : launch_mode<T, MODE_POLY, TRI_NARROW, LAY_KCONT, LAY_KCONT>(gs, n, st);
     case MODE_UPD_ROW:
       if (k.p_sym || k.q_sym) return hipErrorInvalidValue;
-      return launch_mode<T, MODE_UPD_ROW, TRI_NARROW, LAY_KCONT, LAY_NAT>(g, st);
+      return launch_mode<T, MODE_UPD_ROW, TRI_NARROW, LAY_KCONT, LAY_NAT>(gs, n, st);
     case MODE_UPD_COL:
       if (k.p_sym || k.q_sym) return hipErrorInvalidValue;
-      return launch_mode<T, MODE_UPD_COL, TRI_NARROW, LAY_KCONT, LAY_KCONT>(g, st);
+      return launch_mode<T, MODE_UPD_COL, TRI_NARROW, LAY_KCONT, LAY_KCONT>(gs, n, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_gemm(int dtype, const StageKind& k, const GemmArgs& g, hipStream_t st) {
-  if (dtype == 1) return dispatch_mode<bf16>(k, g, st);
-  return dispatch_mode<float>(k, g, st);
+  if (dtype == 1) return dispatch_mode<bf16>(k, &g, 1, st);
+  return dispatch_mode<float>(k, &g, 1, st);
+}
+
+hipError_t launch_gemm_grouped(int dtype, const StageKind& k, const GemmArgs* gs, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (dtype == 1) return dispatch_mode<bf16>(k, gs, n, st);
+  return dispatch_mode<float>(k, gs, n, st);
 }
 
 hipError_t launch_pad(int dtype, const PadArgs& g, hipStream_t st) {
@@ -800,6 +846,22 @@ hipError_t launch_sumsq(int dtype, const NormArgs& g, int batch, hipStream_t st)
   if (dtype == 1) hipLaunchKernelGGL(sumsq_kernel<bf16>, grid, dim3(kNormThreads), 0, st, g);
   else hipLaunchKernelGGL(sumsq_kernel<float>, grid, dim3(kNormThreads), 0, st, g);
   return hipGetLastError();
+}
+
+hipError_t launch_sumsq_grouped(int dtype, const NormArgs* gs, const int* batch, int n, hipStream_t st) {
+  for (int g0 = 0; g0 < n;) {
+    NormLaunch<kMaxLaunchGroups> L{};
+    long long total = 0;
+    const int k = launch_chunk(
+        n - g0, [&](int i) { return (long long)gs[g0 + i].chunks * batch[g0 + i]; }, L.start, &total);
+    for (int i = 0; i < k; ++i) L.a[i] = gs[g0 + i];
+    L.n = k;
+    if (dtype == 1) hipLaunchKernelGGL(sumsq_grouped_kernel<bf16>, dim3((unsigned)total), dim3(kNormThreads), 0, st, L);
+    else hipLaunchKernelGGL(sumsq_grouped_kernel<float>, dim3((unsigned)total), dim3(kNormThreads), 0, st, L);
+    if (hipError_t e = hipGetLastError()) return e;
+    g0 += k;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_scale(int dtype, const NormArgs& g, int batch, hipStream_t st) {

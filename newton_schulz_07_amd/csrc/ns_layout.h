@@ -61,24 +61,27 @@ constexpr TileCfg kTileF32Tri = NS_TILE_F32_TRI;
 constexpr TileCfg kTileF32Rect = NS_TILE_F32_RECT;
 
 // Triangle kernels (Gram, poly) have two bf16 tile shapes: 128 x 128 with
-// two workgroups per CU, and 192 x 192 with one.  A stack with few lower
+// two workgroups per CU, and 192 x 192 with one.  A launch with few lower
 // triangle tiles (fewer than two rounds of 512 workgroup slots at 128) would
 // leave a nearly empty last round, so it takes the larger tile instead
 // (m = 4096: 528 tiles at 128, 253 tiles at 192 on 256 CUs).
-NS_HD constexpr bool use_wide_tri(int dtype, long long batch, long long m) {
-  return dtype == 1 && batch * ((m + 127) / 128) * ((m + 127) / 128 + 1) / 2 < 1024;
+// Lower-triangle tiles of `tile` rows over a stack of m x m results.
+NS_HD constexpr long long tri_tiles(long long batch, long long m, int tile) {
+  return batch * ((m + tile - 1) / tile) * ((m + tile - 1) / tile + 1) / 2;
 }
-// Triangle tile class of a stage: narrow (128), wide (192, see above) or,
-// for the bf16 Gram of a stack with at least four rounds of 256 x 256
+// Triangle tile class of a launch: narrow (128), wide (192, see above) or,
+// for the bf16 Gram of a launch with at least four rounds of 256 x 256
 // triangle tiles, big (256): the Gram has a long K (the long side) and a
 // plain epilogue, so the larger tile's halved operand traffic outweighs its
 // diagonal-tile waste.  The poly keeps 128: its epilogue holds the O_A
-// quads of the whole wave tile in registers.
+// quads of the whole wave tile in registers.  t128 / t256: the launch's
+// triangle tiles at 128 and at 256 (summed over every stack it covers).
 enum TriClass { TRI_NARROW = 0, TRI_WIDE = 1, TRI_BIG = 2 };
+NS_HD constexpr int tri_class_of_tiles(int dtype, long long t128, long long t256, bool gram) {
+  return (dtype == 1 && t128 < 1024) ? TRI_WIDE : (gram && dtype == 1 && t256 >= 1024) ? TRI_BIG : TRI_NARROW;
+}
 NS_HD constexpr int tri_class(int dtype, long long batch, long long m, bool gram) {
-  return use_wide_tri(dtype, batch, m) ? TRI_WIDE
-         : (gram && dtype == 1 && batch * ((m + 255) / 256) * ((m + 255) / 256 + 1) / 2 >= 1024) ? TRI_BIG
-                                                                                                 : TRI_NARROW;
+  return tri_class_of_tiles(dtype, tri_tiles(batch, m, 128), tri_tiles(batch, m, 256), gram);
 }
 NS_HD constexpr TileCfg tile_cfg(int dtype, bool tri, int tri_cls = TRI_NARROW) {
   return dtype == 1 ? (tri ? (tri_cls == TRI_WIDE ? kTileBf16TriWide
@@ -300,6 +303,27 @@ struct GemmArgs {
   int sym_tile;       // stored tile of LAY_SYM operands (rows of the producer's tiles)
 };
 
+// One launch of the MFMA kernel over NG groups of slices: group i covers
+// logical tiles [start[i], start[i + 1]) (the last one up to the grid's
+// end), each with its own shapes, strides and buffers; the tile class and
+// operand layouts are the launch's.  NG = 1 is a plain launch.  The groups
+// travel in the kernel arguments (at most 4 KiB), read with scalar loads.
+constexpr int kMaxLaunchGroups = 16;
+template <int NG> struct GemmLaunch {
+  GemmArgs g[NG];
+  int start[NG];  // first logical tile id of each group; start[0] = 0
+  int n;          // groups in use, 1..NG
+};
+
+// Group of logical tile `lin`: the last group whose first tile is <= lin
+// (a wave-uniform scan, at most kMaxLaunchGroups steps).
+NS_HD int launch_group(int lin, const int* start, int n) {
+  int grp = 0;
+  for (int i = 1; i < n; ++i)
+    if (lin >= start[i]) grp = i;
+  return grp;
+}
+
 // Normalisation: per-slice sum of squares over 32 KiB blocks, then a scale
 // pass over the same blocks.
 struct NormArgs {
@@ -311,6 +335,15 @@ struct NormArgs {
   long long chunk_vecs;  // 16-byte vectors per block
   int chunks;            // blocks per slice
   float eps;
+};
+
+// Sums of squares over NG groups of slices in one launch: block b of the
+// 1-D grid belongs to the last group with start[i] <= b and covers block
+// (b - start[i]) of that group's batch x chunks blocks, slice-major.
+template <int NG> struct NormLaunch {
+  NormArgs a[NG];
+  int start[NG];
+  int n;
 };
 
 }  // namespace ns

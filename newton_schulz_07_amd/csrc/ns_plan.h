@@ -109,6 +109,24 @@ inline NormArgs norm_args(const Plan& p, const void* x, void* y, float* norms, f
   return g;
 }
 
+// Splits groups [0, n) of a grouped launch: the first k of them (at most
+// kMaxLaunchGroups, fewer if the launch's ids would pass 2^30) go into one
+// launch.  units(i) is group i's workgroups; start[i] receives its first id
+// and *total the launch's grid size.  Returns k.
+template <typename Units>
+inline int launch_chunk(int n, Units units, int* start, long long* total) {
+  long long t = 0;
+  int k = 0;
+  for (; k < n && k < kMaxLaunchGroups; ++k) {
+    const long long u = units(k);
+    if (k > 0 && t + u >= (1LL << 30)) break;
+    start[k] = (int)t;
+    t += u;
+  }
+  *total = t;
+  return k;
+}
+
 // Which kernel instance a stage launches.
 struct StageKind {
   int mode;
@@ -117,26 +135,58 @@ struct StageKind {
   bool p_sym = false, q_sym = false;  // LAY_SYM operand (lower block triangle stored)
 };
 
-inline int plan_tri_class(const Plan& p, bool gram) { return tri_class(p.dtype, p.batch, p.m, gram); }
+// Tile classes of the triangle launches of one call.  A call over several
+// stacks (ns_orthogonalize_grouped) runs one Gram launch per orientation
+// (wide stacks read rows of X, tall ones columns) and one poly launch over
+// all of them, so each class follows the tile count of its launch.
+struct TileChoice {
+  int gram_wide, gram_tall;  // Gram class of the wide / tall stacks' launch
+  int poly;                  // poly class (one launch over every stack)
+  // The poly reads A as its lower block triangle (LAY_SYM) and the Gram
+  // stores no mirror: bf16, poly at 128, and every Gram tile a multiple of
+  // the poly's K stage and at least as tall as the poly's tile.
+  // (The kernels instantiate that read for the bf16 poly's 128 tile.)
+  bool lower_only;
+  int gram(bool tall) const { return tall ? gram_tall : gram_wide; }
+};
+
+inline TileChoice choose_tiles(const Plan* ps, int n) {
+  long long t128[2] = {0, 0}, t256[2] = {0, 0};
+  int dtype = n > 0 ? ps[0].dtype : 1;
+  for (int i = 0; i < n; ++i) {
+    const Plan& p = ps[i];
+    t128[p.tall] += tri_tiles(p.batch, p.m, 128);
+    t256[p.tall] += tri_tiles(p.batch, p.m, 256);
+  }
+  TileChoice c;
+  c.gram_wide = tri_class_of_tiles(dtype, t128[0], t256[0], true);
+  c.gram_tall = tri_class_of_tiles(dtype, t128[1], t256[1], true);
+  c.poly = tri_class_of_tiles(dtype, t128[0] + t128[1], t256[0] + t256[1], false);
+  const TileCfg tp = tile_cfg(dtype, true, c.poly);
+  bool ok = dtype == 1 && c.poly == TRI_NARROW;
+  for (int o = 0; o < 2; ++o)
+    if (t128[o] > 0)
+      ok = ok && sym_layout_ok(tp.bm, tile_cfg(dtype, true, c.gram(o != 0)).bm,
+                               tp.cpr * (16 / (int)elem_size(dtype)), tp.st);
+  c.lower_only = ok;
+  return c;
+}
+inline TileChoice choose_tiles(const Plan& p) { return choose_tiles(&p, 1); }
+
+inline int plan_tri_class(const Plan& p, bool gram) {
+  const TileChoice c = choose_tiles(p);
+  return gram ? c.gram(p.tall) : c.poly;
+}
+inline bool gram_lower_only(const Plan& p) { return choose_tiles(p).lower_only; }
 
 // A = X Xᵀ (rows <= cols: rows of X are K-contiguous) or Xᵀ X (rows > cols:
 // columns of X, read in X's natural layout), mirrored into one m x m matrix.
-// The poly can read A as its lower block triangle (LAY_SYM) when the Gram's
-// tile is a multiple of the poly's K stage and at least as tall as the
-// poly's tile; the Gram then stores no mirror.
-// (The kernels instantiate that read for the bf16 poly's 128 tile.)
-inline bool gram_lower_only(const Plan& p) {
-  const TileCfg tg = tile_cfg(p.dtype, true, plan_tri_class(p, true));
-  const TileCfg tp = tile_cfg(p.dtype, true, plan_tri_class(p, false));
-  return p.dtype == 1 && plan_tri_class(p, false) == TRI_NARROW &&
-         sym_layout_ok(tp.bm, tg.bm, tp.cpr * (16 / (int)elem_size(p.dtype)), tp.st);
-}
-
 // mirror: also store the transposes of the off-diagonal tiles (a whole
 // symmetric A); otherwise only the lower block triangle is stored.
-inline GemmArgs gram_args(const Plan& p, const void* x, void* oa, float* da, StageKind* kind,
-                          const float* d_norm = nullptr, bool mirror = true) {
-  const TileCfg t = tile_cfg(p.dtype, true, plan_tri_class(p, true));
+inline GemmArgs gram_args(const Plan& p, const TileChoice& tc, const void* x, void* oa, float* da,
+                          StageKind* kind, const float* d_norm = nullptr, bool mirror = true) {
+  const int cls = tc.gram(p.tall);
+  const TileCfg t = tile_cfg(p.dtype, true, cls);
   GemmArgs g{};
   g.P = g.Q = x;
   g.p_bs = g.q_bs = p.rows * p.cols;
@@ -155,14 +205,18 @@ inline GemmArgs gram_args(const Plan& p, const void* x, void* oa, float* da, Sta
   g.d_norm = d_norm;
   g.norm_n = p.norm_chunks;
   g.eps = kNormEps;
-  *kind = StageKind{MODE_GRAM, p.tall, p.tall, plan_tri_class(p, true)};
+  *kind = StageKind{MODE_GRAM, p.tall, p.tall, cls};
   return g;
+}
+inline GemmArgs gram_args(const Plan& p, const void* x, void* oa, float* da, StageKind* kind,
+                          const float* d_norm = nullptr, bool mirror = true) {
+  return gram_args(p, choose_tiles(p), x, oa, da, kind, d_norm, mirror);
 }
 
 // C = a I + b A + c A A from the split A, written split the same way.
-inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* oc, float* dc, float a,
-                          float b, float c, StageKind* kind) {
-  const TileCfg t = tile_cfg(p.dtype, true, plan_tri_class(p, false));
+inline GemmArgs poly_args(const Plan& p, const TileChoice& tc, const void* oa, const float* da, void* oc,
+                          float* dc, float a, float b, float c, StageKind* kind) {
+  const TileCfg t = tile_cfg(p.dtype, true, tc.poly);
   GemmArgs g{};
   g.P = g.Q = oa;
   g.p_bs = g.q_bs = p.m * p.m;
@@ -183,12 +237,16 @@ inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* 
   g.ca = a;
   g.cb = b;
   g.cc = c;
-  *kind = StageKind{MODE_POLY, false, false, plan_tri_class(p, false)};
-  if (gram_lower_only(p)) {  // read A as its lower block triangle
+  *kind = StageKind{MODE_POLY, false, false, tc.poly};
+  if (tc.lower_only) {  // read A as its lower block triangle
     kind->p_sym = kind->q_sym = true;
-    g.sym_tile = tile_cfg(p.dtype, true, plan_tri_class(p, true)).bm;
+    g.sym_tile = tile_cfg(p.dtype, true, tc.gram(p.tall)).bm;
   }
   return g;
+}
+inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* oc, float* dc, float a,
+                          float b, float c, StageKind* kind) {
+  return poly_args(p, choose_tiles(p), oa, da, oc, dc, a, b, c, kind);
 }
 
 // X' = C X (rows <= cols) or X C (rows > cols), C = O_C + diag(d_C).

@@ -136,3 +136,69 @@ def test_launch_indexes_stay_in_bounds(boundscheck, case):
     r = subprocess.run([boundscheck] + case.split(), capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "violations=0" in r.stdout
+
+
+# ------------------------------------------------- grouped calls (several stacks)
+
+def gcall(shapes, ins=None, outs=None, dtype=1, steps=5, n=None):
+    n = len(shapes) if n is None else n
+    k = len(shapes)
+    ins = ins if ins is not None else [FAKE_IN + (i << 28) for i in range(k)]
+    outs = outs if outs is not None else [FAKE_OUT + (i << 32) for i in range(k)]
+    arr = lambda t, v: (t * max(k, 1))(*v) if k else None
+    b, r, c = ([s[j] for s in shapes] for j in range(3))
+    return ns.lib().ns_orthogonalize_grouped(n, arr(ctypes.c_void_p, ins), arr(ctypes.c_void_p, outs),
+                                             arr(ctypes.c_int64, b), arr(ctypes.c_int64, r),
+                                             arr(ctypes.c_int64, c), dtype, steps, 3.4445, -4.775, 2.0315, None)
+
+
+def test_grouped_empty_calls_are_no_ops():
+    assert gcall([]) == 0
+    assert gcall([(0, 64, 64), (0, 8, 8)], ins=[0, 0], outs=[0, 0]) == 0  # skipped stacks: NULL allowed
+
+
+@pytest.mark.parametrize("kwargs,status,where", [
+    (dict(shapes=[(1, 64, 64)], n=-1), 1, "n_groups"),
+    (dict(shapes=[(1, 64, 64)], n=4097), 1, "n_groups"),
+    (dict(shapes=[(1, 64, 64), (1, 0, 64)]), 1, "stack 1"),
+    (dict(shapes=[(1, 64, 64), (70000, 8, 8)]), 1, "stack 1"),
+    (dict(shapes=[(1, 64, 64)], dtype=5), 2, "dtype"),
+    (dict(shapes=[(1, 64, 64), (1, 64, 64)], ins=[FAKE_IN, FAKE_IN + 8]), 3, "stack 1"),
+    (dict(shapes=[(1, 64, 64)], ins=[0]), 1, "stack 0"),
+    (dict(shapes=[(1, 64, 64)], outs=[FAKE_IN + 64]), 1, "stack 0"),          # partial overlap in/out
+    (dict(shapes=[(1, 64, 64), (1, 64, 64)], outs=[FAKE_OUT, FAKE_IN + (1 << 28)]), 1, "overlaps"),  # out0 = in1
+    (dict(shapes=[(1, 64, 64), (1, 64, 64)], outs=[FAKE_OUT, FAKE_OUT + 4096]), 1, "overlaps"),      # out0 ~ out1
+    (dict(shapes=[(1, 64, 64)], steps=-1), 1, "ns_steps"),
+])
+def test_grouped_argument_errors(kwargs, status, where):
+    st = gcall(**kwargs)
+    assert st == status
+    assert where in ns.lib().ns_last_error().decode()
+
+
+def test_grouped_in_place_and_odd_shapes_pass_the_checks():
+    st = gcall([(2, 264, 520), (3, 100, 37)], outs=[FAKE_IN, FAKE_IN + (1 << 28)])
+    assert st not in (1, 2, 3), ns.lib().ns_last_error().decode()
+
+
+def test_grouped_workspace_is_the_sum_of_the_stacks():
+    shapes = [(2, 264, 520), (3, 520, 264), (1, 100, 37), (0, 64, 64), (16, 1536, 2048)]
+    single = [ns.ns_workspace_bytes(b, r, c, 1) if b else 0 for b, r, c in shapes]
+    assert ns.ns_workspace_bytes_grouped(shapes, 1) == sum(-(-s // 256) * 256 for s in single)
+    assert ns.ns_workspace_bytes_grouped([(1, 0, 8)], 1) == 0
+    assert ns.ns_workspace_bytes_grouped(shapes, 3) == 0
+
+
+@pytest.mark.parametrize("case", [
+    "1 3 2 264 520 3 520 264 1 100 37",          # wide, tall and padded stacks together
+    "0 2 2 264 520 3 520 264 1 33 17",
+    "1 2 200 264 520 200 520 264",               # lower-triangle A, 128 Gram tiles in both orientations
+    "1 2 400 264 520 200 520 264",               # 256 Gram tiles (wide) beside 128 (tall)
+    "1 2 6 264 520 200 520 264",                 # a 192-tile wide Gram beside 128 tall tiles
+    "1 1 " + " ".join(f"{1 + i % 3} {8 + 8 * i} {16 + 8 * ((i * 7) % 13)}" for i in range(20)),  # 20 stacks
+    "1 0 2 64 64 1 9 13",                        # ns_steps = 0
+])
+def test_grouped_launch_indexes_stay_in_bounds(boundscheck, case):
+    r = subprocess.run([boundscheck, "--group"] + case.split(), capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "violations=0" in r.stdout

@@ -92,3 +92,27 @@ def test_full_size_fp32(name):
     errs = run(name, torch.float32)
     report({"case": f"full_fp32_{name}", "errs": errs})
     assert max(errs.values()) <= 1e-3
+
+
+@pytest.mark.parametrize("name", ["iid_256x512", "lowrank64_4096x4096", "experts16_1536x2048",
+                                  "experts128_2048x768"])
+def test_bf16_at_least_as_accurate_as_dense_bf16(name):
+    # [p1] NS microbenchmark table: the symmetric path is no less accurate than
+    # the dense bf16 routine.  The comparator is the same method with dense
+    # bf16 PyTorch matmuls (bench.dense_ns), on the same bf16 input.
+    from bench import dense_ns
+    w = WORKLOADS[name]
+    x = make_workload(name)
+    xg = x.to(torch.bfloat16).to(device())
+    y = ns.orthogonalize(xg)
+    yd = dense_ns(xg)
+    torch.cuda.synchronize()
+    xs = x.reshape(-1, w.rows, w.cols)
+    ys, yds = y.reshape(-1, w.rows, w.cols), yd.reshape(-1, w.rows, w.cols)
+    errs = {}
+    for i in SAMPLES.get(name, [0]):
+        ref = oracle_slice(name, xs[i], i)
+        errs[i] = (float(rel_err(to64(ys[i]), ref)[0]), float(rel_err(to64(yds[i]), ref)[0]))
+    report({"case": f"vs_dense_{name}", "errs_ours_dense": errs})
+    for i, (e, ed) in errs.items():
+        assert e <= ed, (i, e, ed)
