@@ -461,12 +461,18 @@ void replay_gemm_grouped(const std::vector<GemmArgs>& gs, const StageKind& kind,
       return;
     }
     std::vector<std::vector<int>> lins(k);
+    std::vector<int> xcd_tiles(8, 0), xcd_first_group(8, 0);
     for (long long w = 0; w < total; ++w) {
-      const int lin_all = xcd_remap((int)w, (int)total);
-      const int grp = launch_group(lin_all, start, k);
-      if (lin_all < start[grp] || (grp + 1 < k && lin_all >= start[grp + 1]))
-        fail(std::string(what) + ": workgroup mapped to the wrong group");
-      lins[grp].push_back(lin_all - start[grp]);
+      int grp = -1;
+      const int lin = xcd_group_tile((int)w, (int)total, start, k, &grp);
+      if (grp < 0 || grp >= k) {
+        fail(std::string(what) + ": workgroup mapped to no group");
+        continue;
+      }
+      // each XCD walks the groups in order
+      if (grp < xcd_first_group[w % 8]) fail(std::string(what) + ": an XCD goes back to an earlier group");
+      xcd_first_group[w % 8] = grp;
+      lins[grp].push_back(lin);
     }
     for (int i = 0; i < k; ++i) replay_gemm(gs[g0 + i], kind, dtype, coverage, what, &lins[i]);
     g0 += k;
@@ -703,7 +709,47 @@ void replay_grouped_call(int dtype, int steps, const std::vector<Shape>& shapes,
 
 }  // namespace
 
+// The grouped tile map: one group is xcd_remap; for several groups every
+// XCD holds a near-equal share (at most one tile more or less) of each.
+void check_group_map() {
+  for (int G = 1; G <= 2000; ++G) {
+    const int st0[1] = {0};
+    for (int w = 0; w < G; ++w) {
+      int grp = -1;
+      if (xcd_group_tile(w, G, st0, 1, &grp) != xcd_remap(w, G) || grp != 0)
+        fail("xcd_group_tile with one group differs from xcd_remap");
+    }
+  }
+  for (int trial = 0; trial < 200; ++trial) {
+    const int n = 2 + trial % 15;
+    int start[kMaxLaunchGroups];
+    int G = 0;
+    for (int i = 0; i < n; ++i) {
+      start[i] = G;
+      G += 1 + (trial * 7919 + i * 104729) % 997;
+    }
+    std::vector<std::vector<int>> per(n, std::vector<int>(8, 0));
+    std::vector<std::vector<uint8_t>> seen(n);
+    for (int i = 0; i < n; ++i) seen[i].assign((i + 1 < n ? start[i + 1] : G) - start[i], 0);
+    for (int w = 0; w < G; ++w) {
+      int grp = -1;
+      const int lin = xcd_group_tile(w, G, start, n, &grp);
+      if (grp < 0 || grp >= n || lin < 0 || lin >= (int)seen[grp].size() || seen[grp][lin]++) {
+        fail("xcd_group_tile is not a bijection onto the groups' tiles");
+        return;
+      }
+      per[grp][w % 8]++;
+    }
+    for (int i = 0; i < n; ++i) {
+      const int T = (int)seen[i].size();
+      for (int x = 0; x < 8; ++x)
+        if (per[i][x] < T / 8 || per[i][x] > T / 8 + 1) fail("an XCD's share of a group is not T/8 (+1)");
+    }
+  }
+}
+
 int main(int argc, char** argv) {
+  check_group_map();
   // grouped call: --group dtype steps b r c [b r c ...]
   if (argc >= 7 && std::string(argv[1]) == "--group" && (argc - 4) % 3 == 0) {
     const int dtype = std::atoi(argv[2]), steps = std::atoi(argv[3]);

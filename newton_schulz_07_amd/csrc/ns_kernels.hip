@@ -207,10 +207,10 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  const int lin_all = xcd_remap(blockIdx.x, gridDim.x);
-  const int grp = NG > 1 ? launch_group(lin_all, L.start, L.n) : 0;
+  int grp = 0, lin;
+  if constexpr (NG > 1) lin = xcd_group_tile(blockIdx.x, gridDim.x, L.start, L.n, &grp);
+  else lin = xcd_remap(blockIdx.x, gridDim.x);
   const GemmArgs& g = L.g[grp];
-  const int lin = NG > 1 ? lin_all - L.start[grp] : lin_all;
   const int slice = lin / g.tiles_per_slice;
   const int q = lin - slice * g.tiles_per_slice;
   int ti, tj;

@@ -303,11 +303,12 @@ struct GemmArgs {
   int sym_tile;       // stored tile of LAY_SYM operands (rows of the producer's tiles)
 };
 
-// One launch of the MFMA kernel over NG groups of slices: group i covers
-// logical tiles [start[i], start[i + 1]) (the last one up to the grid's
-// end), each with its own shapes, strides and buffers; the tile class and
-// operand layouts are the launch's.  NG = 1 is a plain launch.  The groups
-// travel in the kernel arguments (at most 4 KiB), read with scalar loads.
+// One launch of the MFMA kernel over NG groups of slices: group i has
+// start[i + 1] - start[i] tiles (the last one up to the grid's end), each
+// group its own shapes, strides and buffers; the tile class and operand
+// layouts are the launch's.  NG = 1 is a plain launch.  The groups travel in
+// the kernel arguments (at most 4 KiB), read with scalar loads; workgroups
+// map to (group, tile) through xcd_group_tile.
 constexpr int kMaxLaunchGroups = 16;
 template <int NG> struct GemmLaunch {
   GemmArgs g[NG];
@@ -315,7 +316,36 @@ template <int NG> struct GemmLaunch {
   int n;          // groups in use, 1..NG
 };
 
-// Group of logical tile `lin`: the last group whose first tile is <= lin
+// Workgroup w of a launch over n groups (group i: ids [start[i], start[i+1]),
+// the last one up to G) -> group *grp and tile id within it.  Tiles of
+// different groups cost different amounts (their K differs), so rather than
+// one contiguous range of the launch per XCD (xcd_remap), each XCD (w mod 8)
+// takes a contiguous run of about an eighth of EVERY group, in group order.
+// Group i's T tiles split into eight runs of T / 8, the T % 8 XCDs that take
+// one more being dealt out cyclically from where the previous group's
+// remainder ended; so XCD x's runs add up to exactly its workgroup count,
+// G / 8 (+1 for the first G % 8 XCDs).  With one group this is xcd_remap.
+NS_HD int xcd_group_tile(int w, int G, const int* start, int n, int* grp) {
+  const int x = w % 8;
+  int l = w / 8, o = 0;
+  for (int g = 0; g < n; ++g) {
+    const int T = (g + 1 < n ? start[g + 1] : G) - start[g];
+    const int q = T / 8, r = T % 8;
+    const int p = q + (((x - o + 8) % 8) < r ? 1 : 0);  // this XCD's run of group g
+    if (l < p || g == n - 1) {
+      int before = 0;  // XCDs below x that take one more tile of group g
+      for (int y = 0; y < x; ++y) before += ((y - o + 8) % 8) < r ? 1 : 0;
+      *grp = g;
+      return x * q + before + l;
+    }
+    l -= p;
+    o = (o + r) % 8;
+  }
+  *grp = 0;
+  return 0;
+}
+
+// Group of logical block `lin`: the last group whose first block is <= lin
 // (a wave-uniform scan, at most kMaxLaunchGroups steps).
 NS_HD int launch_group(int lin, const int* start, int n) {
   int grp = 0;
