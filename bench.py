@@ -303,9 +303,10 @@ def all_configs(prefix, steps, warmup):
         print(json.dumps(row), flush=True)
         del xg, out, yd
         torch.cuda.empty_cache()
+    grows = grouped_rows(steps, warmup)
     host = {"cpu_model": cpu_model(), "cores": len(os.sched_getaffinity(0))}
     with open(prefix + ".json", "w") as f:
-        json.dump({"measured_peak": peak, "host": host, "rows": rows}, f, indent=1)
+        json.dump({"measured_peak": peak, "host": host, "rows": rows, "grouped": grows}, f, indent=1)
     lines = ["| workload | dtype | ms/call (p10-p90) | eff. TFLOP/s | % spec peak | % measured peak | dense ms | "
              "speedup vs dense | err max / mean | dense err | model floor | oracle s/slice | H200 dense / QuACK ms |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
@@ -317,9 +318,50 @@ def all_configs(prefix, steps, warmup):
                      f"{r['eff_tflops']:.0f} | {r['pct_spec_peak']:.1f}% | {pm} | {r['dense_ms_per_call']:.3f} | "
                      f"{r['speedup_vs_dense']:.2f}x | {r['err_max']:.2e} / {r['err_mean']:.2e} | "
                      f"{r['dense_err_max']:.2e} | {fl} | {r['oracle_s_per_slice']:.1f} | {h2} |")
+    lines += ["", "Grouped calls (ns_orthogonalize_grouped) vs one ns_orthogonalize call per stack, same inputs "
+              "and stream, median of the timed repetitions of the whole set:", "",
+              "| set | stacks | ms, one call per stack | ms, one grouped call | speedup | bitwise equal |",
+              "|---|---|---|---|---|---|"]
+    for r in grows:
+        lines.append(f"| {r['set']} | {r['stacks']} | {r['singles_ms']:.3f} | {r['grouped_ms']:.3f} | "
+                     f"{r['speedup']:.2f}x | {'yes' if r['bitwise_equal'] else 'NO'} |")
     with open(prefix + ".md", "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines), flush=True)
+
+
+def grouped_rows(steps, warmup):
+    """Each grouped set: the median time of one grouped call over all its
+    stacks and of one call per stack, and whether the outputs agree bitwise."""
+    from ns_inputs import GROUPED_SETS, make_grouped_set
+    rows = []
+    for name, shapes in GROUPED_SETS.items():
+        xs = [x.to("cuda:0") for x in make_grouped_set(name)]
+        ya = [torch.empty_like(x) for x in xs]
+        yb = [torch.empty_like(x) for x in xs]
+
+        def singles():
+            for x, y in zip(xs, ya):
+                ns.orthogonalize(x, out=y)
+
+        def grouped():
+            ns.orthogonalize_grouped(xs, outs=yb)
+
+        res = {}
+        for label, f in (("singles_ms", singles), ("grouped_ms", grouped)):
+            for _ in range(warmup):
+                f()
+            torch.cuda.synchronize()
+            res[label] = float(np.median(call_times(f, max(5, steps // 2))))
+        torch.cuda.synchronize()
+        row = {"set": name, "stacks": "; ".join("x".join(map(str, s)) for s in shapes), **res,
+               "speedup": res["singles_ms"] / res["grouped_ms"],
+               "bitwise_equal": all(torch.equal(a, b) for a, b in zip(ya, yb))}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        del xs, ya, yb
+        torch.cuda.empty_cache()
+    return rows
 
 
 def rounding_floor(name, n):

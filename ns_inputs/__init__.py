@@ -6,9 +6,11 @@ tests and the HIP-side callers use.
 """
 
 from .generators import (  # noqa: F401
+    GROUPED_SETS,
     WORKLOADS,
     Workload,
     gaussian,
+    make_grouped_set,
     make_workload,
     workload_names,
 )

@@ -128,3 +128,27 @@ def make_workload(name):
     if name == "experts128_2048x768":
         return gaussian(w.shape, w.seed, torch.bfloat16)
     raise KeyError(name)
+
+
+# Sets of stacks for the grouped call (several leaf shapes in one call).  The
+# first two use the NS table's sizes: all six of its shapes, and the 4096 and
+# 14336 sizes arranged as one decoder block's matrices (four 4096 x 4096,
+# one 4096 x 14336, two 14336 x 4096).  The leaf sets are synthetic small
+# leaves, where one launch per stage and stack leaves the GPU underfilled.
+# Stack i of a set is iid N(0, 1), seed 1000 + 32 k + i (k: the set's index),
+# bf16.
+GROUPED_SETS = {
+    "ns_table_shapes": [(1, 4096, 4096), (1, 8192, 8192), (1, 4096, 14336), (128, 1536, 2048),
+                        (128, 2048, 768), (32, 7168, 2048)],
+    "block_4096_14336": [(4, 4096, 4096), (1, 4096, 14336), (2, 14336, 4096)],
+    "leaves_768_3072": [(48, 768, 768), (12, 768, 3072), (12, 3072, 768)],
+    "leaves_1024_4096": [(4, 1024, 1024), (1, 1024, 4096), (1, 4096, 1024)],
+    "leaves_24_small": [(1, 512 + 64 * (i % 4), 512 + 128 * (i % 3)) for i in range(24)],
+}
+
+
+def make_grouped_set(name, dtype=torch.bfloat16):
+    """CPU tensors of the named set of stacks."""
+    k = list(GROUPED_SETS).index(name)
+    return [gaussian(s, 1000 + 32 * k + i, dtype) for i, s in enumerate(GROUPED_SETS[name])]
+
