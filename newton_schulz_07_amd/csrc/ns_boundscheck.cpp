@@ -185,14 +185,14 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
   const TileCfg t = tile_cfg(dtype, tri, kind.tri_cls);
   const int es = (int)elem_size(dtype);
   const int EPC = 16 / es, BK = t.cpr * EPC;
-  const int NT = t.wm * t.wn * 64, WTM = t.bm / t.wm, WTN = t.bn / t.wn;
+  const int NT = t.wm * t.wn * 64, WTM = t.bm / t.wm, WTN = t.bn / t.wn;  // threads of the MFMA waves
   const int SM = WTM / 32, SN = WTN / 32;
   const int G = g.tiles_per_slice * g.batch;
   const int nk = (g.K + BK - 1) / BK;
   const int LP = t.bm * t.cpr, LQ = t.bn * t.cpr, STAGE = LP + LQ;
   const int LDS = lds_chunks(t.bm, t.bn, t.cpr, t.st, es);
   const int ERC = epi_row_chunks(t.bn, es), SROW = ERC * EPC;
-  const int NW = t.wm * t.wn, NIW = STAGE / 64 / NW;
+  const int NW = t.wm * t.wn + t.lw, NIW = STAGE / 64 / NW;  // every wave issues loads and stores
 
   if (t.st * STAGE > LDS) fail(std::string(what) + ": the K-stage ring does not fit the LDS array");
   if (STAGE % (64 * NW) != 0 || LP % 64 != 0) fail(std::string(what) + ": stage does not split into wave loads");
@@ -267,7 +267,9 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
     // epilogue operands captured from the K stages (mirrors capture())
     const long long db0 = (long long)slice * g.d_bs;
     const int RCQ = t.bn / EPC;
-    for (int kt = 0; kt < nk && mode != MODE_GRAM; ++kt) {
+    // (a poly with loader waves captures nothing: its epilogue reads O_A)
+    const bool poly_reads_e = mode == MODE_POLY && t.lw > 0;
+    for (int kt = 0; kt < nk && mode != MODE_GRAM && !poly_reads_e; ++kt) {
       const int k0 = kt * BK, slot = kt % t.st;
       if (mode == MODE_POLY && kt >= nat_p) {
         bool any = false;
@@ -341,6 +343,7 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
               if (mode == MODE_POLY) {
                 access(g.d_in, (db + j) * 4, 16, what);
                 access(g.d_in, (db + i) * 4, 4, what);
+                if (poly_reads_e) access(g.E, ((long long)slice * g.e_bs + (long long)i * g.lde + j) * es, qsz, what);
               }
               for (int e = 0; e < 4; ++e)
                 if (i == j + e) {

@@ -177,14 +177,18 @@ __device__ __forceinline__ int nat_lane_byte(int rb, int h, int lane, int rc, fl
 // of the CU's four SIMDs (HIP's second launch bound), which caps the VGPRs.
 // NG > 1: the launch covers up to NG groups of slices of different shapes
 // (GemmLaunch); the workgroup's group is found from its logical tile id.
-template <typename T, int BM, int BN, int WM, int WN, int CPR, int ST, int OCC, int MODE, int PL, int QL, int NG>
-__global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_kernel(const GemmLaunch<NG> L) {
+// LW loader waves join the WM x WN MFMA waves: they issue their share of the
+// K stages' loads and the stores, nothing else.
+template <typename T, int BM, int BN, int WM, int WN, int LW, int CPR, int ST, int OCC, int MODE, int PL, int QL,
+          int NG>
+__global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4) void gemm_kernel(
+    const GemmLaunch<NG> L) {
   // operand layouts (OperandLayout): which read paths each operand needs
   constexpr bool PNAT = PL == LAY_NAT, QNAT = QL == LAY_NAT;
   constexpr bool P_KC = PL != LAY_NAT, P_NT = PL != LAY_KCONT;  // K-contiguous / natural reads of P
   constexpr bool Q_KC = QL != LAY_NAT, Q_NT = QL != LAY_KCONT;
   constexpr bool HAS_SYM = PL == LAY_SYM || QL == LAY_SYM;
-  constexpr int NT = WM * WN * 64, NW = WM * WN;
+  constexpr int NW = WM * WN + LW, NT = NW * 64;  // every wave of the workgroup
   constexpr int EPC = Elem<T>::kChunk;
   constexpr int ES = (int)sizeof(T);
   constexpr int BK = CPR * EPC;
@@ -205,7 +209,8 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
+  const bool mw = LW == 0 || wave < WM * WN;  // an MFMA wave (wave-uniform)
+  const int wm = (mw ? wave : 0) / WN, wn = (mw ? wave : 0) % WN;
 
   int grp = 0, lin;
   if constexpr (NG > 1) lin = xcd_group_tile(blockIdx.x, gridDim.x, L.start, L.n, &grp);
@@ -383,7 +388,10 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
   const float gram_scale = inv_norm * inv_norm;
   const float cb = g.cb, cc = g.cc;
   float drow[SM];
-  QRaw obuf[MODE == MODE_POLY ? SM : 1][MODE == MODE_POLY ? SN : 1][4];
+  // with loader waves the poly's MFMA waves keep no O_A quads (registers):
+  // its epilogue reads O_A from memory instead
+  constexpr bool POLY_CAP = MODE == MODE_POLY && LW == 0;
+  QRaw obuf[POLY_CAP ? SM : 1][POLY_CAP ? SN : 1][4];
   if (MODE == MODE_UPD_ROW) {
 #pragma unroll
     for (int a = 0; a < SM; ++a) {
@@ -391,7 +399,7 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
       drow[a] = i < g.M ? din[i] : 0.0f;
     }
   }
-  if (MODE == MODE_POLY) {
+  if (POLY_CAP) {
 #pragma unroll
     for (int a = 0; a < SM; ++a)
 #pragma unroll
@@ -443,8 +451,8 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
             const int il = wm * WTM + a * 32 + l32;
             const QRaw raw = *reinterpret_cast<const QRaw*>(
                 reinterpret_cast<const T*>(Ps + lds_swz(il, kk / EPC, CPR)) + kk % EPC);
-            if (MODE == MODE_POLY) {
-              obuf[a][b][rg] = raw;
+            if constexpr (MODE == MODE_POLY) {
+              if constexpr (POLY_CAP) obuf[a][b][rg] = raw;
             } else {
               float x[4];
               Quad<T>::unpack(raw, x);
@@ -477,10 +485,11 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
     else wait_vm_lgkm0<0>();
     ring_barrier();
     if (kt + ST - 1 < nk) issue(kt + ST - 1, (u + ST - 1) % ST);
+    if (!mw) return;
     compute(u, pn, qn);
     // the poly's O_A capture happens at the stage covering the tile's own
     // columns, left of its diagonal, where P is K-contiguous
-    if constexpr (MODE != MODE_GRAM && !(MODE == MODE_POLY && decltype(pn)::value)) capture(u, kt);
+    if constexpr (MODE != MODE_GRAM && !(MODE == MODE_POLY && (decltype(pn)::value || !POLY_CAP))) capture(u, kt);
   };
   auto phase = [&](int kt_begin, int kt_end, auto pn, auto qn) __attribute__((always_inline)) {  // kt_begin % ST == 0
     int kt0 = kt_begin;
@@ -527,50 +536,57 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
   T* S = reinterpret_cast<T*>(lds);
   constexpr int SROW = ERC * EPC;  // staged row stride in elements
 
+  if (mw) {
 #pragma unroll
-  for (int a = 0; a < SM; ++a) {
-    const int il = wm * WTM + a * 32 + acc_i(lane);
-    const int i = i0 + il;
+    for (int a = 0; a < SM; ++a) {
+      const int il = wm * WTM + a * 32 + acc_i(lane);
+      const int i = i0 + il;
 #pragma unroll
-    for (int b = 0; b < SN; ++b)
+      for (int b = 0; b < SN; ++b)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int jl = wn * WTN + b * 32 + acc_j(rg, lane);
-        const int j = j0 + jl;
-        if (i >= g.M || j >= g.N) continue;  // N % 8 == 0: j..j+3 all valid
-        float v[4] = {acc[a][b][4 * rg], acc[a][b][4 * rg + 1], acc[a][b][4 * rg + 2], acc[a][b][4 * rg + 3]};
-        float w[4];
-        if (MODE == MODE_GRAM) {
+        for (int rg = 0; rg < 4; ++rg) {
+          const int jl = wn * WTN + b * 32 + acc_j(rg, lane);
+          const int j = j0 + jl;
+          if (i >= g.M || j >= g.N) continue;  // N % 8 == 0: j..j+3 all valid
+          float v[4] = {acc[a][b][4 * rg], acc[a][b][4 * rg + 1], acc[a][b][4 * rg + 2], acc[a][b][4 * rg + 3]};
+          float w[4];
+          if (MODE == MODE_GRAM) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            w[e] = v[e] * gram_scale;
-            if (i == j + e) {
-              dout[i] = w[e];
-              w[e] = 0.0f;
+            for (int e = 0; e < 4; ++e) {
+              w[e] = v[e] * gram_scale;
+              if (i == j + e) {
+                dout[i] = w[e];
+                w[e] = 0.0f;
+              }
             }
-          }
-        } else if (MODE == MODE_POLY) {
-          float o[4];
-          Quad<T>::unpack(obuf[a][b][rg], o);
-          const float4 dj = *reinterpret_cast<const float4*>(din + j);
-          const float dje[4] = {dj.x, dj.y, dj.z, dj.w};
-          const float di = din[i];
+          } else if (MODE == MODE_POLY) {
+            float o[4];
+            if constexpr (POLY_CAP)
+              Quad<T>::unpack(obuf[a][b][rg], o);
+            else
+              Quad<T>::unpack(*reinterpret_cast<const QRaw*>(reinterpret_cast<const T*>(g.E) + (size_t)slice * g.e_bs +
+                                                             (size_t)i * g.lde + j),
+                              o);
+            const float4 dj = *reinterpret_cast<const float4*>(din + j);
+            const float dje[4] = {dj.x, dj.y, dj.z, dj.w};
+            const float di = din[i];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // b O_A + c (O_A O_A + (d_i + d_j) O_A); diagonal: a + b d_i + c ((O_A O_A)_ii + d_i^2)
-            w[e] = fmaf(cb, o[e], cc * fmaf(di + dje[e], o[e], v[e]));
-            if (i == j + e) {
-              dout[i] = fmaf(cc, fmaf(di, di, v[e]), fmaf(cb, di, g.ca));
-              w[e] = 0.0f;
+            for (int e = 0; e < 4; ++e) {
+              // b O_A + c (O_A O_A + (d_i + d_j) O_A); diagonal: a + b d_i + c ((O_A O_A)_ii + d_i^2)
+              w[e] = fmaf(cb, o[e], cc * fmaf(di + dje[e], o[e], v[e]));
+              if (i == j + e) {
+                dout[i] = fmaf(cc, fmaf(di, di, v[e]), fmaf(cb, di, g.ca));
+                w[e] = 0.0f;
+              }
             }
-          }
-        } else {
-          // d_C ⊙ X was added to the accumulators in the K loop
+          } else {
+            // d_C ⊙ X was added to the accumulators in the K loop
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = v[e] * inv_norm;
+            for (int e = 0; e < 4; ++e) w[e] = v[e] * inv_norm;
+          }
+          *reinterpret_cast<typename Quad<T>::Raw*>(S + il * SROW + jl) = Quad<T>::pack(w);
         }
-        *reinterpret_cast<typename Quad<T>::Raw*>(S + il * SROW + jl) = Quad<T>::pack(w);
-      }
+    }
   }
   __syncthreads();
 
@@ -761,12 +777,12 @@ __global__ __launch_bounds__(256) void pad_kernel(const PadArgs g) {
 template <typename T, int MODE, int CLS, int PL, int QL>
 static hipError_t launch_mode(const GemmArgs* gs, int n, hipStream_t st) {
   constexpr TileCfg t = tile_cfg(std::is_same<T, bf16>::value ? 1 : 0, mode_is_tri(MODE), CLS);
-  const dim3 block(t.wm * t.wn * 64);
+  const dim3 block((t.wm * t.wn + t.lw) * 64);
   if (n == 1) {
     GemmLaunch<1> L{};
     L.g[0] = gs[0];
     L.n = 1;
-    hipLaunchKernelGGL((gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.cpr, t.st, t.occ, MODE, PL, QL, 1>),
+    hipLaunchKernelGGL((gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.lw, t.cpr, t.st, t.occ, MODE, PL, QL, 1>),
                        dim3(gs[0].tiles_per_slice * gs[0].batch), block, 0, st, L);
     return hipGetLastError();
   }
@@ -778,7 +794,7 @@ static hipError_t launch_mode(const GemmArgs* gs, int n, hipStream_t st) {
         n - g0, [&](int i) { return (long long)gs[g0 + i].tiles_per_slice * gs[g0 + i].batch; }, L.start, &total);
     for (int i = 0; i < k; ++i) L.g[i] = gs[g0 + i];
     L.n = k;
-    hipLaunchKernelGGL((gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.cpr, t.st, t.occ, MODE, PL, QL, kMaxLaunchGroups>),
+    hipLaunchKernelGGL((gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.lw, t.cpr, t.st, t.occ, MODE, PL, QL, kMaxLaunchGroups>),
                        dim3((unsigned)total), block, 0, st, L);
     if (hipError_t e = hipGetLastError()) return e;
     g0 += k;

@@ -33,13 +33,14 @@ NS_HD constexpr bool mode_is_tri(int mode) { return mode == MODE_GRAM || mode ==
 // for.
 struct TileCfg {
   int bm, bn, wm, wn, cpr, st, occ;
+  int lw = 0;  // loader waves: extra waves that only issue the K stages' loads and join the stores
 };
 
 #ifndef NS_TILE_BF16_TRI
 #define NS_TILE_BF16_TRI {128, 128, 2, 4, 8, 2, 2}
 #endif
 #ifndef NS_TILE_BF16_TRI_WIDE
-#define NS_TILE_BF16_TRI_WIDE {192, 192, 2, 2, 8, 2, 1}
+#define NS_TILE_BF16_TRI_WIDE {192, 192, 2, 2, 8, 2, 1, 4}
 #endif
 #ifndef NS_TILE_BF16_TRI_BIG
 #define NS_TILE_BF16_TRI_BIG {256, 256, 2, 4, 8, 2, 1}
@@ -65,6 +66,12 @@ constexpr TileCfg kTileF32Rect = NS_TILE_F32_RECT;
 // triangle tiles (fewer than two rounds of 512 workgroup slots at 128) would
 // leave a nearly empty last round, so it takes the larger tile instead
 // (m = 4096: 528 tiles at 128, 253 tiles at 192 on 256 CUs).
+// The 192 tile runs 4 MFMA waves (one per SIMD, 96 x 96 each) beside 4
+// loader waves: a workgroup's rate of LDS-direct loads grows with the number
+// of waves issuing them (from L2, about 22 B/clk per CU with 4 waves and 35
+// with 8), and the 192 tile needs a byte per 96 flops, which 4 waves alone
+// cannot feed.  Its poly then reads O_A in the epilogue instead of holding
+// the captured quads in registers.
 // Lower-triangle tiles of `tile` rows over a stack of m x m results.
 NS_HD constexpr long long tri_tiles(long long batch, long long m, int tile) {
   return batch * ((m + tile - 1) / tile) * ((m + tile - 1) / tile + 1) / 2;
