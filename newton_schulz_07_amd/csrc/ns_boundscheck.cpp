@@ -256,10 +256,17 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
       for (int b : {nat_p - 1, nat_p, nat_q - 1, nat_q})
         if (b > 0 && b < nk - 1) kst.push_back(b);
     }
+    // a diagonal Gram tile (2-slot ring) loads the P rows only, spread over
+    // every wave, and reads its Q fragments from the P region: the operands
+    // must be the same rows of the same matrix
+    const bool dshare = mode == MODE_GRAM && t.st == 2 && ti == tj;
+    if (dshare && (g.P != g.Q || g.ldp != g.ldq || g.p_bs != g.q_bs || i0 != j0 || t.bm != t.bn || NIW % 2 ||
+                   kind.p_nat != kind.q_nat || NW * (NIW / 2) * 64 != t.bm * t.cpr))  // ... and cover every P chunk
+      fail(std::string(what) + ": diagonal tile shares operands that differ");
     for (int kt : kst)
       for (int wave = 0; wave < NW; ++wave)
-        replay_dma(wave, NIW, t, es, kt >= nat_p, kt >= nat_q, kt * BK, g, slice, i0, j0, STAGE, kt % t.st, LDS,
-                   what);
+        replay_dma(wave, dshare ? NIW / 2 : NIW, t, es, kt >= nat_p, kt >= nat_q, kt * BK, g, slice, i0, j0, STAGE,
+                   kt % t.st, LDS, what);
     // norm folded into the first step: the slice's partial sums of squares
     if (mode != MODE_POLY && g.d_norm != nullptr)
       for (int i = 0; i < g.norm_n; ++i) access(g.d_norm, ((long long)slice * g.norm_n + i) * 4, 4, what);

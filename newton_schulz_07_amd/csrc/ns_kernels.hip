@@ -253,6 +253,20 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
     src_off[t] = src_of(dma_src(idx, lane, BM, BN, CPR, EPC, PNAT, QNAT, ES), idx * 64 < LP ? PNAT : QNAT);
     if constexpr (HAS_SYM) src_alt[t] = src_of(dma_src(idx, lane, BM, BN, CPR, EPC, true, true, ES), true);
   }
+  // A diagonal Gram tile reads the same rows as P and as Q: its stages load
+  // the P rows only, spread over every wave, and its Q fragments are read
+  // from the P region.  (The 2-slot ring waits for all of a wave's loads at
+  // every stage, so a wave's load count may differ between tiles.)
+  constexpr bool DSH = MODE == MODE_GRAM && ST == 2;
+  constexpr int NIP = NIW / 2;  // P loads per wave, spread over every wave
+  static_assert(!DSH || (BM == BN && NIP * 2 == NIW), "diagonal sharing needs square tiles");
+  const bool dshare = DSH && ti == tj;
+  unsigned src_dg[DSH ? NIP : 1];
+  if constexpr (DSH) {
+#pragma unroll
+    for (int t = 0; t < NIP; ++t)
+      src_dg[t] = src_of(dma_src(wave * NIP + t, lane, BM, BN, CPR, EPC, PNAT, QNAT, ES), PNAT);
+  }
   const unsigned step_kc = (unsigned)(BK * ES);
   const unsigned step_np = (unsigned)(BK * g.ldp * ES), step_nq = (unsigned)(BK * g.ldq * ES);
   // Loads of stage kt into ring slot `slot`.  When the whole stage lies
@@ -269,7 +283,15 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
       const bool alt = HAS_SYM && (is_p ? PL == LAY_SYM : QL == LAY_SYM) && nat;
       return (alt ? src_alt[HAS_SYM ? t : 0] : src_off[t]) + (unsigned)kt * (nat ? (is_p ? step_np : step_nq) : step_kc);
     };
-    if (k0 + BK <= g.K) {
+    if (DSH && dshare) {
+#pragma unroll
+      for (int t = 0; t < (DSH ? NIP : 1); ++t) {
+        const int idx = wave * NIP + t;  // P chunks only
+        const unsigned off = src_dg[DSH ? t : 0] + (unsigned)kt * (PNAT ? step_np : step_kc);
+        const int kpos = dma_src(idx, lane, BM, BN, CPR, EPC, PNAT, QNAT, ES).kpos;
+        dma16(lds_addr(lds + slot * STAGE + idx * 64), (k0 + BK <= g.K || k0 + kpos < g.K) ? off : kOutOfRange, rP);
+      }
+    } else if (k0 + BK <= g.K) {
 #pragma unroll
       for (int t = 0; t < NIW; ++t) {
         const int idx = wave * NIW + t;  // wave-uniform
@@ -326,6 +348,18 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
     for (int b = 0; b < SN; ++b)
 #pragma unroll
       for (int h = 0; h < NH; ++h) natq[b][h] = nat_lane_byte(wn * WTN + 32 * b, h, lane, RCQ, T()) + QOFF;
+  }
+  if (DSH && dshare) {  // Q fragments from the P region (same rows)
+    if constexpr (Q_KC) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kcq[s] -= QOFF;
+    }
+    if constexpr (Q_NT) {
+#pragma unroll
+      for (int b = 0; b < SN; ++b)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) natq[b][h] -= QOFF;
+    }
   }
   const char* lb = reinterpret_cast<const char*>(lds);
   // fragments of step s; pn / qn (std::integral_constant) select the natural
