@@ -303,6 +303,115 @@ int check_grouped(int n, const void* const* in, void* const* out, const int64_t*
   return NS_OK;
 }
 
+// The method on the non-empty stacks gs (plans, workspace offsets and the
+// caller's pointers set), sharing each stage's launches among them: per step
+// one Gram launch per orientation (wide stacks read rows of X, tall ones
+// columns), one poly launch over all and one update per orientation.  Odd
+// shapes run on zero-padded copies (see ns_plan.h); an in-place call with an
+// odd step count starts from a copy of the input.  With no step each stack
+// is normalised on its own (sum of squares, then scale).  *tc and launches
+// (Gram, poly, update launches of one step) describe what ran.
+int run_stacks(std::vector<Group>& gs, size_t ws_bytes, int ns_steps, float a, float b, float c, hipStream_t st,
+               ns::TileChoice* tc, int launches[3]) {
+  const int dtype = gs[0].p.dtype;
+  char* ws = nullptr;
+  if (int s = get_workspace(st, ws_bytes, &ws)) return s;
+  std::vector<Plan> plans;
+  for (Group& g : gs) {
+    char* w = ws + g.ws_off;
+    g.in = g.uin;
+    g.out = g.uout;
+    g.xtmp = w + g.p.off_xtmp;
+    g.oa = w + g.p.off_oa;
+    g.oc = w + g.p.off_oc;
+    g.da = reinterpret_cast<float*>(w + g.p.off_da);
+    g.dc = reinterpret_cast<float*>(w + g.p.off_dc);
+    g.part = reinterpret_cast<float*>(w + g.p.off_part);
+    plans.push_back(g.p);
+  }
+  const int n = (int)gs.size();
+  *tc = ns::choose_tiles(plans.data(), n);
+  launches[0] = launches[1] = launches[2] = 0;
+
+  for (Group& g : gs) {
+    if (g.p.padded) {
+      const ns::PadArgs pa = ns::pad_args(g.p, g.uin, ws + g.ws_off + g.p.off_pin, true);
+      if (int s = check_hip(ns::launch_pad(dtype, pa, st), "pad launch")) return s;
+      g.in = ws + g.ws_off + g.p.off_pin;
+      g.out = ws + g.ws_off + g.p.off_pout;
+    }
+    g.copy_in = ns::input_copy_needed(ns_steps, g.in == g.out);
+  }
+  if (ns_steps == 0) {  // X0 = x / (||x||_F + eps), in place if out == in
+    for (const Group& g : gs)
+      if (int s = run_normalize(g.in, g.out, nullptr, g.p, g.part, st)) return s;
+  } else {
+    // one sum-of-squares launch over every stack; 1/||x|| rides in step 1
+    std::vector<NormArgs> na;
+    std::vector<int> nb;
+    for (const Group& g : gs) {
+      na.push_back(ns::norm_args(g.p, g.in, nullptr, nullptr, g.part));
+      nb.push_back((int)g.p.batch);
+    }
+    if (int s = check_hip(timed_launch(NS_KIND_SUMSQ, st,
+                                       [&] { return ns::launch_sumsq_grouped(dtype, na.data(), nb.data(), n, st); }),
+                          "sum-of-squares launch"))
+      return s;
+    for (const Group& g : gs)
+      if (g.copy_in) {
+        const size_t pb = (size_t)g.p.batch * g.p.rows * g.p.cols * esize(dtype);
+        if (int s = check_hip(hipMemcpyAsync(g.xtmp, g.in, pb, hipMemcpyDeviceToDevice, st), "input copy")) return s;
+      }
+  }
+  auto buf = [&](const Group& g, int s) -> const void* {
+    if (s == 0) return g.copy_in ? g.xtmp : g.in;
+    return ns::iterate_in_out(ns_steps, s) ? g.out : g.xtmp;
+  };
+  auto wbuf = [&](const Group& g, int s) -> void* { return ns::iterate_in_out(ns_steps, s) ? g.out : g.xtmp; };
+  auto launch = [&](int kind, const char* what, const ns::StageKind& k, const std::vector<GemmArgs>& ga) {
+    return check_hip(
+        timed_launch(kind, st, [&] { return ns::launch_gemm_grouped(dtype, k, ga.data(), (int)ga.size(), st); }),
+        what);
+  };
+  for (int s = 1; s <= ns_steps; ++s) {
+    const bool first = s == 1;  // the Gram and the update of step 1 see the raw input
+    for (int o = 0; o < 2; ++o) {  // Gram: wide stacks, then tall ones
+      std::vector<GemmArgs> ga;
+      ns::StageKind k{};
+      for (const Group& g : gs)
+        if (g.p.tall == (o == 1))
+          ga.push_back(ns::gram_args(g.p, *tc, buf(g, s - 1), g.oa, g.da, &k, first ? g.part : nullptr,
+                                     !tc->lower_only));
+      if (ga.empty()) continue;
+      launches[0] += first;
+      if (int e = launch(NS_KIND_GRAM, "gram launch", k, ga)) return e;
+    }
+    {
+      std::vector<GemmArgs> ga;
+      ns::StageKind k{};
+      for (const Group& g : gs) ga.push_back(ns::poly_args(g.p, *tc, g.oa, g.da, g.oc, g.dc, a, b, c, &k));
+      launches[1] += first;
+      if (int e = launch(NS_KIND_POLY, "poly launch", k, ga)) return e;
+    }
+    for (int o = 0; o < 2; ++o) {  // update: wide stacks, then tall ones
+      std::vector<GemmArgs> ga;
+      ns::StageKind k{};
+      for (const Group& g : gs)
+        if (g.p.tall == (o == 1))
+          ga.push_back(ns::update_args(g.p, buf(g, s - 1), g.oc, g.dc, wbuf(g, s), &k, first ? g.part : nullptr));
+      if (ga.empty()) continue;
+      launches[2] += first;
+      if (int e = launch(NS_KIND_UPDATE, "update launch", k, ga)) return e;
+    }
+  }
+  for (const Group& g : gs)
+    if (g.p.padded) {
+      const ns::PadArgs pa = ns::pad_args(g.p, g.out, g.uout, false);
+      if (int s = check_hip(ns::launch_pad(dtype, pa, st), "unpad launch")) return s;
+    }
+  return NS_OK;
+}
+
 void record_config_grouped(const std::vector<Group>& gs, const ns::TileChoice& tc, int steps, int launches[3]) {
   const int dtype = gs[0].p.dtype;
   int nt = 0;
@@ -345,51 +454,16 @@ int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows, int
   if (batch == 0) return NS_OK;
   if (int s = check_arch()) return s;
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const Plan p = make_plan(batch, rows, cols, dtype);
-  char* ws = nullptr;
-  if (int s = get_workspace(st, p.total, &ws)) return s;
-  void* xtmp = ws + p.off_xtmp;
-  void* oa = ws + p.off_oa;
-  void* oc = ws + p.off_oc;
-  float* da = reinterpret_cast<float*>(ws + p.off_da);
-  float* dc = reinterpret_cast<float*>(ws + p.off_dc);
-  float* part = reinterpret_cast<float*>(ws + p.off_part);
-
-  // odd shapes: the method runs on zero-padded copies (see ns_plan.h)
-  const void* uin = in;
-  void* uout = out;
-  if (p.padded) {
-    const ns::PadArgs pa = ns::pad_args(p, uin, ws + p.off_pin, true);
-    if (int s = check_hip(ns::launch_pad(dtype, pa, st), "pad launch")) return s;
-    in = ws + p.off_pin;
-    out = ws + p.off_pout;
-  }
-  const size_t pbytes = (size_t)p.batch * p.rows * p.cols * esize(dtype);
-
-  const bool fold = ns::fold_normalisation(ns_steps);
-  const bool copy_in = ns::input_copy_needed(ns_steps, in == out);
-  auto buf = [&](int s) -> const void* {
-    if (s == 0 && fold) return copy_in ? xtmp : in;
-    return ns::iterate_in_out(ns_steps, s) ? out : xtmp;
-  };
-  auto wbuf = [&](int s) -> void* { return ns::iterate_in_out(ns_steps, s) ? out : xtmp; };
-
-  // folded: sums of squares only; otherwise (no step) X0 = x / (||x|| + eps)
-  if (int s = run_normalize(in, fold ? nullptr : wbuf(0), nullptr, p, part, st)) return s;
-  if (copy_in)  // out == in, odd steps: X_0 is a copy of the input (see ns_plan.h)
-    if (int s = check_hip(hipMemcpyAsync(xtmp, in, pbytes, hipMemcpyDeviceToDevice, st), "input copy")) return s;
-  for (int s = 1; s <= ns_steps; ++s) {
-    const float* dn = (fold && s == 1) ? part : nullptr;  // partial sums of squares -> ||x||_F
-    // the poly reads A as its lower block triangle when it can (no mirror)
-    if (int e = run_gram(buf(s - 1), oa, da, p, st, dn, !ns::gram_lower_only(p))) return e;
-    if (int e = run_poly(oa, da, oc, dc, p, a, b, c, st)) return e;
-    if (int e = run_update(buf(s - 1), oc, dc, wbuf(s), p, st, dn)) return e;
-  }
-  if (p.padded) {
-    const ns::PadArgs pa = ns::pad_args(p, out, uout, false);
-    if (int s = check_hip(ns::launch_pad(dtype, pa, st), "unpad launch")) return s;
-  }
+  std::vector<Group> gs(1);
+  gs[0].p = make_plan(batch, rows, cols, dtype);
+  gs[0].ws_off = 0;
+  gs[0].uin = in;
+  gs[0].uout = out;
+  ns::TileChoice tc;
+  int launches[3];
+  if (int s = run_stacks(gs, gs[0].p.total, ns_steps, a, b, c, static_cast<hipStream_t>(stream), &tc, launches))
+    return s;
+  const Plan& p = gs[0].p;
   record_config(p, ns_steps);
   return NS_OK;
 }
@@ -407,120 +481,15 @@ int ns_orthogonalize_grouped(int n_groups, const void* const* in, void* const* o
   const size_t total = plan_groups(n_groups, batch, rows, cols, dtype, &gs);
   if (gs.empty()) return NS_OK;
   if (int s = check_arch()) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (ns_steps == 0) {  // normalisation only: the stacks one after another
-    for (int i = 0; i < n_groups; ++i)
-      if (batch[i] > 0)
-        if (int s = ns_orthogonalize(in[i], out[i], batch[i], rows[i], cols[i], dtype, 0, a, b, c, stream))
-          return fail(s, "stack " + std::to_string(i) + ": " + t_err);
-    t_cfg = "grouped: " + std::to_string(gs.size()) + " stacks, ns_steps=0: normalised one by one";
-    return NS_OK;
+  for (int i = 0, k = 0; i < n_groups; ++i) {
+    if (batch[i] == 0) continue;
+    gs[k].uin = in[i];
+    gs[k].uout = out[i];
+    ++k;
   }
-  char* ws = nullptr;
-  if (int s = get_workspace(st, total, &ws)) return s;
-  {
-    int k = 0;
-    for (int i = 0; i < n_groups; ++i) {
-      if (batch[i] == 0) continue;
-      Group& g = gs[k++];
-      char* w = ws + g.ws_off;
-      g.uin = in[i];
-      g.uout = out[i];
-      g.in = in[i];
-      g.out = out[i];
-      g.xtmp = w + g.p.off_xtmp;
-      g.oa = w + g.p.off_oa;
-      g.oc = w + g.p.off_oc;
-      g.da = reinterpret_cast<float*>(w + g.p.off_da);
-      g.dc = reinterpret_cast<float*>(w + g.p.off_dc);
-      g.part = reinterpret_cast<float*>(w + g.p.off_part);
-    }
-  }
-  const int n = (int)gs.size();
-  std::vector<Plan> plans;
-  for (const Group& g : gs) plans.push_back(g.p);
-  const ns::TileChoice tc = ns::choose_tiles(plans.data(), n);
-
-  // odd shapes run on zero-padded copies; in-place calls with an odd step
-  // count start from a copy of the input (as in ns_orthogonalize)
-  for (Group& g : gs) {
-    if (g.p.padded) {
-      const ns::PadArgs pa = ns::pad_args(g.p, g.uin, ws + g.ws_off + g.p.off_pin, true);
-      if (int s = check_hip(ns::launch_pad(dtype, pa, st), "pad launch")) return s;
-      g.in = ws + g.ws_off + g.p.off_pin;
-      g.out = ws + g.ws_off + g.p.off_pout;
-    }
-    g.copy_in = ns::input_copy_needed(ns_steps, g.in == g.out);
-  }
-  // one sum-of-squares launch over every stack (the norm is folded into step 1)
-  {
-    std::vector<NormArgs> na;
-    std::vector<int> nb;
-    for (const Group& g : gs) {
-      na.push_back(ns::norm_args(g.p, g.in, nullptr, nullptr, g.part));
-      nb.push_back((int)g.p.batch);
-    }
-    if (int s = check_hip(timed_launch(NS_KIND_SUMSQ, st,
-                                       [&] { return ns::launch_sumsq_grouped(dtype, na.data(), nb.data(), n, st); }),
-                          "sum-of-squares launch"))
-      return s;
-  }
-  for (const Group& g : gs)
-    if (g.copy_in) {
-      const size_t pb = (size_t)g.p.batch * g.p.rows * g.p.cols * esize(dtype);
-      if (int s = check_hip(hipMemcpyAsync(g.xtmp, g.in, pb, hipMemcpyDeviceToDevice, st), "input copy")) return s;
-    }
-  auto buf = [&](const Group& g, int s) -> const void* {
-    if (s == 0) return g.copy_in ? g.xtmp : g.in;
-    return ns::iterate_in_out(ns_steps, s) ? g.out : g.xtmp;
-  };
-  auto wbuf = [&](const Group& g, int s) -> void* { return ns::iterate_in_out(ns_steps, s) ? g.out : g.xtmp; };
-  int launches[3] = {0, 0, 0};
-  for (int s = 1; s <= ns_steps; ++s) {
-    const bool first = s == 1;
-    for (int o = 0; o < 2; ++o) {  // Gram: wide stacks, then tall ones
-      std::vector<GemmArgs> ga;
-      ns::StageKind k{};
-      for (const Group& g : gs)
-        if (g.p.tall == (o == 1))
-          ga.push_back(ns::gram_args(g.p, tc, buf(g, s - 1), g.oa, g.da, &k, first ? g.part : nullptr,
-                                     !tc.lower_only));
-      if (ga.empty()) continue;
-      launches[0] += s == 1;
-      if (int e = check_hip(timed_launch(NS_KIND_GRAM, st,
-                                         [&] { return ns::launch_gemm_grouped(dtype, k, ga.data(), (int)ga.size(), st); }),
-                            "gram launch"))
-        return e;
-    }
-    {
-      std::vector<GemmArgs> ga;
-      ns::StageKind k{};
-      for (const Group& g : gs) ga.push_back(ns::poly_args(g.p, tc, g.oa, g.da, g.oc, g.dc, a, b, c, &k));
-      launches[1] += s == 1;
-      if (int e = check_hip(timed_launch(NS_KIND_POLY, st,
-                                         [&] { return ns::launch_gemm_grouped(dtype, k, ga.data(), n, st); }),
-                            "poly launch"))
-        return e;
-    }
-    for (int o = 0; o < 2; ++o) {  // update: wide stacks, then tall ones
-      std::vector<GemmArgs> ga;
-      ns::StageKind k{};
-      for (const Group& g : gs)
-        if (g.p.tall == (o == 1))
-          ga.push_back(ns::update_args(g.p, buf(g, s - 1), g.oc, g.dc, wbuf(g, s), &k, first ? g.part : nullptr));
-      if (ga.empty()) continue;
-      launches[2] += s == 1;
-      if (int e = check_hip(timed_launch(NS_KIND_UPDATE, st,
-                                         [&] { return ns::launch_gemm_grouped(dtype, k, ga.data(), (int)ga.size(), st); }),
-                            "update launch"))
-        return e;
-    }
-  }
-  for (const Group& g : gs)
-    if (g.p.padded) {
-      const ns::PadArgs pa = ns::pad_args(g.p, g.out, g.uout, false);
-      if (int s = check_hip(ns::launch_pad(dtype, pa, st), "unpad launch")) return s;
-    }
+  ns::TileChoice tc;
+  int launches[3];
+  if (int s = run_stacks(gs, total, ns_steps, a, b, c, static_cast<hipStream_t>(stream), &tc, launches)) return s;
   record_config_grouped(gs, tc, ns_steps, launches);
   return NS_OK;
 }

@@ -899,6 +899,7 @@ hipError_t launch_sumsq(int dtype, const NormArgs& g, int batch, hipStream_t st)
 }
 
 hipError_t launch_sumsq_grouped(int dtype, const NormArgs* gs, const int* batch, int n, hipStream_t st) {
+  if (n == 1) return launch_sumsq(dtype, gs[0], batch[0], st);  // the plain (slice, block) grid
   for (int g0 = 0; g0 < n;) {
     NormLaunch<kMaxLaunchGroups> L{};
     long long total = 0;
