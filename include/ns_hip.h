@@ -93,7 +93,9 @@ enum {
  * yields zeros.  NaN/Inf inputs propagate; they are not checked.
  * Internally the Gram matrix A and the polynomial C = aI + bA + cAA are held
  * as an off-diagonal matrix (zero diagonal) in `dtype` plus an fp32 diagonal
- * vector; only lower-triangle tiles of both are computed and mirrored.
+ * vector; only lower-triangle tiles of both are computed.  C is mirrored;
+ * A is mirrored too, except on large bf16 stacks, where it is kept as its
+ * lower block triangle and the polynomial reads the rest transposed.
  * The workspace (ns_workspace_bytes) is allocated on first use per
  * (device, stream) and grown when needed; growing synchronises the device.
  */
@@ -172,7 +174,7 @@ int ns_query_last_config(char* buf, size_t n);
 enum {
   NS_KIND_SUMSQ = 0,   /* per-slice sum of squares (norm, pass 1)        */
   NS_KIND_SCALE = 1,   /* scale and cast (norm, pass 2)                   */
-  NS_KIND_GRAM = 2,    /* lower-triangle X Xᵀ with mirror                 */
+  NS_KIND_GRAM = 2,    /* lower-triangle X Xᵀ (mirrored or lower-only)    */
   NS_KIND_POLY = 3,    /* lower-triangle C = aI + bA + cAA with mirror     */
   NS_KIND_UPDATE = 4,  /* X' = C X (or X C for tall), diagonal folded     */
   NS_KIND_COUNT = 5

@@ -173,8 +173,9 @@ __device__ __forceinline__ int nat_lane_byte(int rb, int h, int lane, int rc, fl
   return nat_lane_byte_f32(rb, h, lane, rc);
 }
 
-// OCC workgroups of WM x WN waves per CU: at least OCC WM WN / 4 waves on each
-// of the CU's four SIMDs (HIP's second launch bound), which caps the VGPRs.
+// OCC workgroups of WM x WN + LW waves per CU: at least OCC (WM WN + LW) / 4
+// waves on each of the CU's four SIMDs (HIP's second launch bound), which
+// caps the VGPRs.
 // NG > 1: the launch covers up to NG groups of slices of different shapes
 // (GemmLaunch); the workgroup's group is found from its logical tile id.
 // LW loader waves join the WM x WN MFMA waves: they issue their share of the

@@ -18,7 +18,8 @@ namespace ns {
 
 // Work modes of the tiled MFMA kernel.
 enum GemmMode : int {
-  MODE_GRAM = 0,    // lower-triangle tiles of P Pᵀ, mirrored, diagonal split
+  MODE_GRAM = 0,    // lower-triangle tiles of P Pᵀ, diagonal split; mirrored unless
+                    // stored as the lower block triangle (out_t null)
   MODE_POLY = 1,    // lower-triangle tiles of b A + c A A (+ a on diagonal)
   MODE_UPD_ROW = 2, // rectangle tiles of O_C X + d_C[row] * X
   MODE_UPD_COL = 3  // rectangle tiles of X O_C + d_C[col] * X
