@@ -10,14 +10,17 @@ value       effective bf16 TFLOP/s of the primary workload: dense-equivalent
             FLOPs 5 (4 m² n + 2 m³) per slice divided by the measured time
             (the comparison basis of the prime-rl NS microbenchmark table)
 roofline    the dominant kernel (the update product) timed with HIP events
-            around each of its launches on the launch stream, algorithmic
-            FLOPs per launch / mean launch time, against the 2.5 PFLOP/s dense
-            bf16 MFMA peak
+            in its dispatch packets on the launch stream, in the timed
+            region (the third of the five update launches of every timed
+            call), algorithmic FLOPs per launch / mean launch time, against
+            the 2.5 PFLOP/s dense bf16 MFMA peak and the measured peak
 cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
 dense       the same method with dense PyTorch-ROCm bf16 matmuls (hipBLASLt),
             timed on the same inputs: the comparator column of the pages'
             dense-vs-symmetric table (bench only, not a library path)
-measured_peak  a plain 4096^3 bf16 torch.matmul (hipBLASLt) on this GPU
+measured_peak  the bf16 MFMA rate of a register-only loop on this GPU and the
+            shader clock it ran at (ns_peak_mfma), with a plain 4096^3
+            torch.matmul (hipBLASLt) beside it as a library GEMM reference
 """
 
 import argparse
@@ -136,7 +139,10 @@ def time_dense(xg, steps, warmup):
 
 
 def measured_peak(reps=20):
-    """TFLOP/s of a plain 4096^3 bf16 torch.matmul (hipBLASLt) on this GPU."""
+    """Measured bf16 matrix peaks on this GPU: the library's register-only
+    MFMA loop (ns_peak_mfma: the rate and shader clock the matrix cores hold
+    under full load), and a plain 4096^3 torch.matmul (hipBLASLt) as a
+    library GEMM reference."""
     n = 4096
     g = torch.Generator(device="cuda:0").manual_seed(0)
     a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
@@ -145,8 +151,14 @@ def measured_peak(reps=20):
         torch.matmul(a, b)
     torch.cuda.synchronize()
     ts = call_times(lambda: torch.matmul(a, b), reps)
-    return {"what": "torch.matmul bf16 4096x4096x4096 (hipBLASLt)",
-            "tflops": 2 * n ** 3 / (float(np.median(ts)) * 1e-3) / 1e12}
+    gemm = 2 * n ** 3 / (float(np.median(ts)) * 1e-3) / 1e12
+    ns.ns_peak_mfma("bf16", 1 << 16)  # warm-up
+    runs = [ns.ns_peak_mfma("bf16", 1 << 20) for _ in range(3)]
+    tf, mhz = max(runs)
+    return {"what": "register-only v_mfma_f32_32x32x16_bf16 loop, 2 workgroups of 4 waves per CU (ns_peak_mfma), "
+                    "best of 3 runs of ~0.1 s",
+            "tflops": tf, "shader_clock_mhz": mhz,
+            "gemm_reference": {"what": "torch.matmul bf16 4096x4096x4096 (hipBLASLt)", "tflops": gemm}}
 
 
 def cpu_model():
@@ -172,6 +184,10 @@ def time_workload(name, steps, warmup, kernel_mask):
         ns.orthogonalize(xg, out=out)
     torch.cuda.synchronize()
     ns.ns_timing_reset()
+    # one timed launch per kernel kind and call (the third of the call's five
+    # launches of a step kernel): each timed dispatch releases its events at
+    # its end, which delays the next kernel by a few microseconds
+    ns.ns_timing_sample(STEPS_NS, STEPS_NS // 2)
     ns.ns_timing_enable(kernel_mask)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -181,8 +197,8 @@ def time_workload(name, steps, warmup, kernel_mask):
     stop.record()
     torch.cuda.synchronize()
     ns.ns_timing_enable(0)
+    ns.ns_timing_sample(1, 0)
     ms = start.elapsed_time(stop) / steps
-    ns.ns_timing_enable(0)
     per_call = spread(call_times(lambda: ns.orthogonalize(xg, out=out), steps))
     kernels = {}
     for kind, kname in ns.KIND_NAMES.items():
@@ -380,7 +396,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed calls per workload first: the shader clock ramps up over the first tens of ms")
     ap.add_argument("--workload", default="lowrank64_4096x4096", choices=list(WORKLOADS))
     ap.add_argument("--also", nargs="*", default=["experts128_1536x2048"])
     ap.add_argument("--kernel-timing", choices=["dominant", "all", "none"], default="dominant")
@@ -422,6 +439,7 @@ def main():
     y_dense = None
     for r in [main_run] + extra:
         r["pct_measured_peak"] = 100.0 * r["eff_tflops"] / peak["tflops"]
+        r["pct_hipblaslt_gemm"] = 100.0 * r["eff_tflops"] / peak["gemm_reference"]["tflops"]
         if not args.no_dense:
             d, yd = time_dense(r["xg"], max(3, args.steps // 2), 2)
             r["dense"] = {**d, "eff_tflops": r["eff_tflops"] * r["ms_per_call"] / d["ms_per_call"],
@@ -440,7 +458,10 @@ def main():
         roof = {"bound": "mfma", "kernel": "gemm_kernel update (X' = C X)", "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "traffic": tr["bytes"] if tr else None, "traffic_detail": tr,
-                "mean_launch_ms": upd["mean_ms"], "algorithmic_flops_per_launch": algo["update"],
+                "measured_peak": peak["tflops"], "frac_of_measured_peak": achieved / peak["tflops"],
+                "mean_launch_ms": upd["mean_ms"], "timed_launches": upd["launches"],
+                "timed_launch_sample": "the third update of each timed call (HIP events in the dispatch packet)",
+                "algorithmic_flops_per_launch": algo["update"],
                 "kernel_source_hash": kernel_source_hash()}
 
     cpu = None
@@ -453,7 +474,7 @@ def main():
 
     def summary(r):
         keys = ("name", "shape", "ms_per_call", "p10_ms", "median_ms", "p90_ms", "eff_tflops", "pct_dense_bf16_peak",
-                "pct_measured_peak", "dense", "kernels")
+                "pct_measured_peak", "pct_hipblaslt_gemm", "dense", "kernels")
         return {k: r[k] for k in keys if k in r}
 
     line = {

@@ -166,8 +166,16 @@ int ns_query_last_config(char* buf, size_t n);
 /*
  * Per-kernel timing with HIP events on the launch stream.
  * ns_timing_enable(mask): from now on, every launch of a kernel whose kind
- * bit is set in `mask` (1 << NS_KIND_*) is bracketed by two hipEvents on its
- * stream; 0 disables.  ns_timing_reset() drops the records.
+ * bit is set in `mask` (1 << NS_KIND_*) records two hipEvents in its own
+ * dispatch packet (hipExtLaunchKernel: the kernel's start and end), so no
+ * packet goes between the kernels of a call; 0 disables.  The events are
+ * timing-only (no system-scope fence), so timed kernels run as they do
+ * untimed; the stream must be synchronised before their results are read on
+ * the host.
+ * ns_timing_sample(every, offset): time only launch i of each kind (counted
+ * from the last reset) with i % every == offset; every = 1, offset = 0 (the
+ * default) times them all.  NS_ERR_INVALID_ARG unless 0 <= offset < every.
+ * ns_timing_reset() drops the records and restarts the launch counts.
  * ns_timing_query(kind, &total_ms, &launches) waits for the recorded events
  * and returns the summed kernel time and the number of launches recorded.
  */
@@ -180,8 +188,24 @@ enum {
   NS_KIND_COUNT = 5
 };
 int ns_timing_enable(int mask);
+int ns_timing_sample(int every, int offset);
 int ns_timing_reset(void);
 int ns_timing_query(int kind, double* total_ms, int64_t* launches);
+
+/*
+ * Roofline calibration on the current device (a measurement helper; no step
+ * of the method): every wave of two workgroups per CU runs `iters` (a
+ * multiple of 4, at most 2^30) rounds of four back-to-back MFMAs on
+ * registers only, v_mfma_f32_32x32x16_bf16 (dtype 1) or
+ * v_mfma_f32_32x32x2_f32 (dtype 0), with operands that change from one
+ * instruction to the next.  Writes the achieved dense rate in TFLOP/s (HIP
+ * events on `stream`) and the average shader clock in MHz over the loop
+ * (s_memtime against the constant-rate s_memrealtime).  Allocates and frees
+ * its own small buffers and synchronises with the stream; about 0.1 s at
+ * iters = 2^20.  Errors: NS_ERR_DTYPE, NS_ERR_INVALID_ARG (null outputs,
+ * iters out of range), NS_ERR_ARCH, NS_ERR_HIP.
+ */
+int ns_peak_mfma(int dtype, int64_t iters, double* tflops, double* clock_mhz, void* stream);
 
 /* ---- single stages (the same kernels ns_orthogonalize runs) ------------- */
 /* Shapes: a slice of x is rows x cols, both multiples of 8 (the stages do

@@ -37,8 +37,10 @@ SIGNATURES = {
     "ns_last_error": (ctypes.c_char_p, []),
     "ns_query_last_config": (_int, [ctypes.c_char_p, _sz]),
     "ns_timing_enable": (_int, [_int]),
+    "ns_timing_sample": (_int, [_int, _int]),
     "ns_timing_reset": (_int, []),
     "ns_timing_query": (_int, [_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
+    "ns_peak_mfma": (_int, [_int, _i64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), _vp]),
     "ns_stage_normalize": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]),
     "ns_stage_gram": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]),
     "ns_stage_poly": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _flt, _flt, _flt, _vp]),
@@ -201,6 +203,11 @@ def ns_timing_enable(mask):
     _check(lib().ns_timing_enable(int(mask)))
 
 
+def ns_timing_sample(every=1, offset=0):
+    """Time only launch i of each kind with i % every == offset."""
+    _check(lib().ns_timing_sample(int(every), int(offset)))
+
+
 def ns_timing_reset():
     _check(lib().ns_timing_reset())
 
@@ -211,6 +218,18 @@ def ns_timing_query(kind):
     n = ctypes.c_int64()
     _check(lib().ns_timing_query(int(kind), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def ns_peak_mfma(dtype="bf16", iters=1 << 20, stream=None):
+    """(TFLOP/s, MHz): the dense MFMA rate of a register-only loop on the
+    current device and the average shader clock during it."""
+    import torch
+    code = {"bf16": NS_DTYPE_BF16, "fp32": NS_DTYPE_F32}[dtype]
+    st = stream if stream is not None else torch.cuda.current_stream()
+    tf = ctypes.c_double()
+    mhz = ctypes.c_double()
+    _check(lib().ns_peak_mfma(code, int(iters), ctypes.byref(tf), ctypes.byref(mhz), ctypes.c_void_p(st.cuda_stream)))
+    return tf.value, mhz.value
 
 
 # ------------------------------------------------------------------ stages

@@ -133,6 +133,8 @@ struct TimingRec {
 };
 std::mutex g_t_mu;
 int g_t_mask = 0;
+int g_t_every = 1, g_t_offset = 0;     // launch i of a kind is timed when i % every == offset
+int64_t g_t_count[NS_KIND_COUNT] = {};  // launches of each kind since the last reset
 std::vector<TimingRec> g_t_recs;
 std::vector<hipEvent_t> g_t_pool;
 
@@ -142,27 +144,40 @@ hipEvent_t take_event() {
     g_t_pool.pop_back();
     return e;
   }
+  // Timing-only events: no system-scope fence when recorded.  With the
+  // default flags every record writes back and invalidates the caches, which
+  // costs the timed kernels time of their own and slows the kernel after
+  // them.  Their timestamps are only read after the stream has been
+  // synchronised (ns_timing_query).
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
+// The events travel in the kernel's dispatch packet (ns::set_launch_events),
+// so timing adds no packets between the kernels of a call.
 template <typename F>
 hipError_t timed_launch(int kind, hipStream_t st, F&& f) {
   std::unique_lock<std::mutex> lk(g_t_mu);
-  const bool on = (g_t_mask >> kind) & 1;
+  const bool on = ((g_t_mask >> kind) & 1) && g_t_count[kind]++ % g_t_every == g_t_offset;
   hipEvent_t a = nullptr, b = nullptr;
   if (on) {
     a = take_event();
     b = take_event();
-    if (a && b) (void)hipEventRecord(a, st);
   }
   lk.unlock();
+  const bool timed = on && a && b;
+  if (timed) ns::set_launch_events(a, b);
   hipError_t e = f();
-  if (on && a && b) {
-    (void)hipEventRecord(b, st);
+  if (on) {
+    ns::set_launch_events(nullptr, nullptr);
     lk.lock();
-    g_t_recs.push_back(TimingRec{kind, a, b});
+    if (timed && e == hipSuccess) {
+      g_t_recs.push_back(TimingRec{kind, a, b});
+    } else {  // nothing recorded them: back to the pool
+      if (a) g_t_pool.push_back(a);
+      if (b) g_t_pool.push_back(b);
+    }
   }
   return e;
 }
@@ -553,8 +568,19 @@ int ns_timing_enable(int mask) {
   return NS_OK;
 }
 
+int ns_timing_sample(int every, int offset) {
+  t_err.clear();
+  if (every < 1 || offset < 0 || offset >= every)
+    return fail(NS_ERR_INVALID_ARG, "timing sample needs every >= 1 and 0 <= offset < every");
+  std::lock_guard<std::mutex> lk(g_t_mu);
+  g_t_every = every;
+  g_t_offset = offset;
+  return NS_OK;
+}
+
 int ns_timing_reset(void) {
   std::lock_guard<std::mutex> lk(g_t_mu);
+  for (auto& c : g_t_count) c = 0;
   for (auto& r : g_t_recs) {
     g_t_pool.push_back(r.a);
     g_t_pool.push_back(r.b);
@@ -643,6 +669,67 @@ int ns_stage_update(const void* x, const void* c_off, const float* c_diag, void*
   if (int s = check_arch()) return s;
   const Plan p = make_plan(batch, rows, cols, dtype);
   return run_update(x, c_off, c_diag, x_out, p, static_cast<hipStream_t>(stream));
+}
+
+int ns_peak_mfma(int dtype, int64_t iters, double* tflops, double* clock_mhz, void* stream) {
+  t_err.clear();
+  if (int s = check_dtype(dtype)) return s;
+  if (tflops == nullptr || clock_mhz == nullptr) return fail(NS_ERR_INVALID_ARG, "tflops and clock_mhz must be non-NULL");
+  if (iters < 4 || iters > (int64_t(1) << 30) || iters % 4 != 0)
+    return fail(NS_ERR_INVALID_ARG, "iters must be a multiple of 4 in [4, 2^30]");
+  if (int s = check_arch()) return s;
+  int dev = 0, cus = 0, wall_khz = 0;
+  if (int s = check_hip(hipGetDevice(&dev), "hipGetDevice")) return s;
+  if (int s = check_hip(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "CU count")) return s;
+  if (int s = check_hip(hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev), "wall clock rate"))
+    return s;
+  // two workgroups of four waves per CU: two waves on each SIMD
+  const int blocks = 2 * cus;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* sink = nullptr;
+  unsigned long long* clocks = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  int status = NS_OK;
+  auto cleanup = [&]() {
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (sink) (void)hipFree(sink);
+    if (clocks) (void)hipFree(clocks);
+  };
+  if ((status = check_hip(hipMalloc(&sink, sizeof(float) * blocks * ns::kPeakThreads), "hipMalloc")) ||
+      (status = check_hip(hipMalloc(&clocks, sizeof(unsigned long long) * 4 * blocks), "hipMalloc")) ||
+      (status = check_hip(hipEventCreate(&e0), "hipEventCreate")) ||
+      (status = check_hip(hipEventCreate(&e1), "hipEventCreate")) ||
+      (status = check_hip(hipEventRecord(e0, st), "hipEventRecord")) ||
+      (status = check_hip(ns::launch_mfma_peak(dtype, blocks, (int)iters, sink, clocks, st), "peak launch")) ||
+      (status = check_hip(hipEventRecord(e1, st), "hipEventRecord")) ||
+      (status = check_hip(hipEventSynchronize(e1), "hipEventSynchronize"))) {
+    cleanup();
+    return status;
+  }
+  float ms = 0.0f;
+  std::vector<unsigned long long> c(4 * (size_t)blocks);
+  if ((status = check_hip(hipEventElapsedTime(&ms, e0, e1), "hipEventElapsedTime")) ||
+      (status = check_hip(hipMemcpy(c.data(), clocks, c.size() * sizeof(c[0]), hipMemcpyDeviceToHost), "hipMemcpy"))) {
+    cleanup();
+    return status;
+  }
+  cleanup();
+  const double waves = (double)blocks * ns::kPeakThreads / 64.0;
+  const double flops = waves * (double)iters * ns::mfma_peak_acc() * (double)ns::mfma_peak_flops_per_inst(dtype);
+  *tflops = ms > 0.0f ? flops / (ms * 1e-3) / 1e12 : 0.0;
+  // average over workgroups of (shader cycles / wall ticks) x wall rate
+  double ratio = 0.0;
+  int n = 0;
+  for (int b = 0; b < blocks; ++b) {
+    const unsigned long long dt = c[4 * b + 1] - c[4 * b], dr = c[4 * b + 3] - c[4 * b + 2];
+    if (dr > 0) {
+      ratio += (double)dt / (double)dr;
+      ++n;
+    }
+  }
+  *clock_mhz = n ? ratio / n * wall_khz / 1000.0 : 0.0;
+  return NS_OK;
 }
 
 }  // extern "C"

@@ -20,6 +20,7 @@
 //   poly:               P = Q = rows of O_A  (A symmetric: A A = A Aᵀ)
 //   update, wide:       P = rows of O_C, Q = columns of X (X' = C X)
 //   update, tall:       P = rows of X,   Q = rows of O_C  (X' = X C)
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -806,6 +807,27 @@ __global__ __launch_bounds__(256) void pad_kernel(const PadArgs g) {
 
 // ------------------------------------------------------------- launchers
 
+// Timing events of the launches this thread makes next (set_launch_events).
+// They ride in the dispatch itself (hipExtLaunchKernelGGL): the start event
+// takes the first dispatch's start, the stop event every dispatch's end (the
+// last one stands), and no marker packet goes between the kernels.
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+void set_launch_events(hipEvent_t start, hipEvent_t stop) {
+  t_ev_start = start;
+  t_ev_stop = stop;
+}
+
+template <typename K, typename... A>
+static void dispatch(K kernel, dim3 grid, dim3 block, hipStream_t st, A... args) {
+  if (t_ev_start == nullptr && t_ev_stop == nullptr) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+    return;
+  }
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, st, t_ev_start, t_ev_stop, 0, args...);
+  t_ev_start = nullptr;  // a later launch of the same kind moves only the stop
+}
+
 // A launch over the groups gs[0 .. n): one group is a plain launch (NG = 1);
 // several go out kMaxLaunchGroups at a time, each launch's grid covering the
 // tiles of its groups.
@@ -817,8 +839,8 @@ static hipError_t launch_mode(const GemmArgs* gs, int n, hipStream_t st) {
     GemmLaunch<1> L{};
     L.g[0] = gs[0];
     L.n = 1;
-    hipLaunchKernelGGL((gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.lw, t.cpr, t.st, t.occ, MODE, PL, QL, 1>),
-                       dim3(gs[0].tiles_per_slice * gs[0].batch), block, 0, st, L);
+    dispatch(gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.lw, t.cpr, t.st, t.occ, MODE, PL, QL, 1>,
+             dim3(gs[0].tiles_per_slice * gs[0].batch), block, st, L);
     return hipGetLastError();
   }
   static_assert(sizeof(GemmLaunch<kMaxLaunchGroups>) <= 4096, "kernel arguments over 4 KiB");
@@ -829,8 +851,8 @@ static hipError_t launch_mode(const GemmArgs* gs, int n, hipStream_t st) {
         n - g0, [&](int i) { return (long long)gs[g0 + i].tiles_per_slice * gs[g0 + i].batch; }, L.start, &total);
     for (int i = 0; i < k; ++i) L.g[i] = gs[g0 + i];
     L.n = k;
-    hipLaunchKernelGGL((gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.lw, t.cpr, t.st, t.occ, MODE, PL, QL, kMaxLaunchGroups>),
-                       dim3((unsigned)total), block, 0, st, L);
+    dispatch(gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.lw, t.cpr, t.st, t.occ, MODE, PL, QL, kMaxLaunchGroups>,
+             dim3((unsigned)total), block, st, L);
     if (hipError_t e = hipGetLastError()) return e;
     g0 += k;
   }
@@ -887,15 +909,15 @@ hipError_t launch_pad(int dtype, const PadArgs& g, hipStream_t st) {
   const long long total = g.batch * (g.to_padded ? g.rows * g.cols : g.urows * g.ucols);
   const long long want = (total + 255) / 256;
   const unsigned blocks = (unsigned)(want < 65536 ? (want > 0 ? want : 1) : 65536);
-  if (dtype == 1) hipLaunchKernelGGL(pad_kernel<bf16>, dim3(blocks), dim3(256), 0, st, g);
-  else hipLaunchKernelGGL(pad_kernel<float>, dim3(blocks), dim3(256), 0, st, g);
+  if (dtype == 1) dispatch(pad_kernel<bf16>, dim3(blocks), dim3(256), st, g);
+  else dispatch(pad_kernel<float>, dim3(blocks), dim3(256), st, g);
   return hipGetLastError();
 }
 
 hipError_t launch_sumsq(int dtype, const NormArgs& g, int batch, hipStream_t st) {
   dim3 grid(g.chunks, batch);
-  if (dtype == 1) hipLaunchKernelGGL(sumsq_kernel<bf16>, grid, dim3(kNormThreads), 0, st, g);
-  else hipLaunchKernelGGL(sumsq_kernel<float>, grid, dim3(kNormThreads), 0, st, g);
+  if (dtype == 1) dispatch(sumsq_kernel<bf16>, grid, dim3(kNormThreads), st, g);
+  else dispatch(sumsq_kernel<float>, grid, dim3(kNormThreads), st, g);
   return hipGetLastError();
 }
 
@@ -908,8 +930,8 @@ hipError_t launch_sumsq_grouped(int dtype, const NormArgs* gs, const int* batch,
         n - g0, [&](int i) { return (long long)gs[g0 + i].chunks * batch[g0 + i]; }, L.start, &total);
     for (int i = 0; i < k; ++i) L.a[i] = gs[g0 + i];
     L.n = k;
-    if (dtype == 1) hipLaunchKernelGGL(sumsq_grouped_kernel<bf16>, dim3((unsigned)total), dim3(kNormThreads), 0, st, L);
-    else hipLaunchKernelGGL(sumsq_grouped_kernel<float>, dim3((unsigned)total), dim3(kNormThreads), 0, st, L);
+    if (dtype == 1) dispatch(sumsq_grouped_kernel<bf16>, dim3((unsigned)total), dim3(kNormThreads), st, L);
+    else dispatch(sumsq_grouped_kernel<float>, dim3((unsigned)total), dim3(kNormThreads), st, L);
     if (hipError_t e = hipGetLastError()) return e;
     g0 += k;
   }
@@ -918,8 +940,8 @@ hipError_t launch_sumsq_grouped(int dtype, const NormArgs* gs, const int* batch,
 
 hipError_t launch_scale(int dtype, const NormArgs& g, int batch, hipStream_t st) {
   dim3 grid(g.chunks, batch);
-  if (dtype == 1) hipLaunchKernelGGL(scale_kernel<bf16>, grid, dim3(kNormThreads), 0, st, g);
-  else hipLaunchKernelGGL(scale_kernel<float>, grid, dim3(kNormThreads), 0, st, g);
+  if (dtype == 1) dispatch(scale_kernel<bf16>, grid, dim3(kNormThreads), st, g);
+  else dispatch(scale_kernel<float>, grid, dim3(kNormThreads), st, g);
   return hipGetLastError();
 }
 

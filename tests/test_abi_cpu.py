@@ -105,6 +105,22 @@ def test_timing_query_rejects_bad_kind():
     assert L.ns_timing_query(99, ctypes.byref(ms), ctypes.byref(n)) == 1
     assert L.ns_timing_reset() == 0
     assert L.ns_timing_query(2, ctypes.byref(ms), ctypes.byref(n)) == 0 and n.value == 0
+    for every, offset in ((0, 0), (5, 5), (5, -1), (-1, 0)):
+        assert L.ns_timing_sample(every, offset) == 1, (every, offset)
+    assert L.ns_timing_sample(5, 2) == 0
+    assert L.ns_timing_sample(1, 0) == 0
+
+
+def test_peak_calibration_argument_errors():
+    # every check runs before the device is touched
+    L = ns.lib()
+    tf, mhz = ctypes.c_double(), ctypes.c_double()
+    assert L.ns_peak_mfma(7, 1024, ctypes.byref(tf), ctypes.byref(mhz), None) == 2  # NS_ERR_DTYPE
+    assert L.ns_peak_mfma(1, 1024, None, ctypes.byref(mhz), None) == 1
+    assert L.ns_peak_mfma(1, 1024, ctypes.byref(tf), None, None) == 1
+    for iters in (0, 3, 1026, (1 << 30) + 4):
+        assert L.ns_peak_mfma(1, iters, ctypes.byref(tf), ctypes.byref(mhz), None) == 1, iters
+        assert "iters" in L.ns_last_error().decode()
 
 
 def test_python_binding_rejects_cpu_tensors():
