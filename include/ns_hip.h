@@ -193,6 +193,16 @@ int ns_timing_reset(void);
 int ns_timing_query(int kind, double* total_ms, int64_t* launches);
 
 /*
+ * Diagnostic: with on != 0, every later ns_orthogonalize and
+ * ns_orthogonalize_grouped call first fills its whole workspace with 0xFF
+ * bytes (NaN in bf16 and in fp32) on its stream, so that any kernel reading
+ * a workspace element that no earlier kernel of the call wrote turns the
+ * result into NaN.  0 turns it off (the default).  For tests: it costs one
+ * fill of the workspace per call.  Returns NS_OK.
+ */
+int ns_set_workspace_poison(int on);
+
+/*
  * Roofline calibration on the current device (a measurement helper; no step
  * of the method): every wave of two workgroups per CU runs `iters` (a
  * multiple of 4, at most 2^30) rounds of four back-to-back MFMAs on

@@ -40,6 +40,7 @@ SIGNATURES = {
     "ns_timing_sample": (_int, [_int, _int]),
     "ns_timing_reset": (_int, []),
     "ns_timing_query": (_int, [_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
+    "ns_set_workspace_poison": (_int, [_int]),
     "ns_peak_mfma": (_int, [_int, _i64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), _vp]),
     "ns_stage_normalize": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]),
     "ns_stage_gram": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]),
@@ -218,6 +219,11 @@ def ns_timing_query(kind):
     n = ctypes.c_int64()
     _check(lib().ns_timing_query(int(kind), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def ns_set_workspace_poison(on):
+    """Fill every later call's workspace with NaN bytes first (diagnostic)."""
+    _check(lib().ns_set_workspace_poison(1 if on else 0))
 
 
 def ns_peak_mfma(dtype="bf16", iters=1 << 20, stream=None):

@@ -7,6 +7,7 @@
 // "Summary" item 2, and param-decomp PR #978, "What").
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cstdio>
 #include <cstring>
 #include <map>
@@ -326,11 +327,15 @@ int check_grouped(int n, const void* const* in, void* const* out, const int64_t*
 // odd step count starts from a copy of the input.  With no step each stack
 // is normalised on its own (sum of squares, then scale).  *tc and launches
 // (Gram, poly, update launches of one step) describe what ran.
+std::atomic<int> g_poison{0};  // ns_set_workspace_poison
+
 int run_stacks(std::vector<Group>& gs, size_t ws_bytes, int ns_steps, float a, float b, float c, hipStream_t st,
                ns::TileChoice* tc, int launches[3]) {
   const int dtype = gs[0].p.dtype;
   char* ws = nullptr;
   if (int s = get_workspace(st, ws_bytes, &ws)) return s;
+  if (g_poison.load() && ws_bytes > 0)
+    if (int s = check_hip(hipMemsetAsync(ws, 0xFF, ws_bytes, st), "workspace poison fill")) return s;
   std::vector<Plan> plans;
   for (Group& g : gs) {
     char* w = ws + g.ws_off;
@@ -669,6 +674,11 @@ int ns_stage_update(const void* x, const void* c_off, const float* c_diag, void*
   if (int s = check_arch()) return s;
   const Plan p = make_plan(batch, rows, cols, dtype);
   return run_update(x, c_off, c_diag, x_out, p, static_cast<hipStream_t>(stream));
+}
+
+int ns_set_workspace_poison(int on) {
+  g_poison.store(on != 0);
+  return NS_OK;
 }
 
 int ns_peak_mfma(int dtype, int64_t iters, double* tflops, double* clock_mhz, void* stream) {
