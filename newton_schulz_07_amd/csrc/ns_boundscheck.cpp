@@ -350,7 +350,18 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
               if (mode == MODE_POLY) {
                 access(g.d_in, (db + j) * 4, 16, what);
                 access(g.d_in, (db + i) * 4, 4, what);
-                if (poly_reads_e) access(g.E, ((long long)slice * g.e_bs + (long long)i * g.lde + j) * es, qsz, what);
+                if (poly_reads_e) {
+                  const long long e0 = (long long)slice * g.e_bs + (long long)i * g.lde + j;
+                  access(g.E, e0 * es, qsz, what);
+                  // (a lower-triangle A: the element must be one the Gram stored)
+                  auto wr = g_written.find(reinterpret_cast<uintptr_t>(g.E));
+                  if (wr != g_written.end())
+                    for (int e = 0; e < qsz / es; ++e)
+                      if (wr->second[e0 + e] != 1) {
+                        fail(std::string(what) + ": poly epilogue reads an element of A the Gram did not write");
+                        break;
+                      }
+                }
               }
               for (int e = 0; e < 4; ++e)
                 if (i == j + e) {
