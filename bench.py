@@ -9,6 +9,8 @@ the whole workload, inputs already resident in HBM.  Prints ONE JSON line.
 value       effective bf16 TFLOP/s of the primary workload: dense-equivalent
             FLOPs 5 (4 m² n + 2 m³) per slice divided by the measured time
             (the comparison basis of the prime-rl NS microbenchmark table)
+norm_pass   the sum-of-squares pass (HBM-bound): bytes read per launch over
+            its mean HIP-event launch time, against 8 TB/s
 roofline    the dominant kernel (the update product) timed with HIP events
             in its dispatch packets on the launch stream, in the timed
             region (the third of the five update launches of every timed
@@ -432,7 +434,9 @@ def main():
         all_configs(args.all_configs, args.steps, args.warmup)
         return
 
-    mask = {"dominant": 1 << ns.NS_KIND_UPDATE, "all": 0x1F, "none": 0}[args.kernel_timing]
+    # the dominant kernel and the HBM-bound norm pass
+    mask = {"dominant": (1 << ns.NS_KIND_UPDATE) | (1 << ns.NS_KIND_SUMSQ), "all": 0x1F,
+            "none": 0}[args.kernel_timing]
     main_run = time_workload(args.workload, args.steps, args.warmup, mask)
     extra = [time_workload(n, args.steps, args.warmup, mask) for n in args.also if n != args.workload]
     peak = measured_peak()
@@ -463,6 +467,16 @@ def main():
                 "timed_launch_sample": "the third update of each timed call (HIP events in the dispatch packet)",
                 "algorithmic_flops_per_launch": algo["update"],
                 "kernel_source_hash": kernel_source_hash()}
+
+    # the norm pass (sum of squares) reads the input once: HBM-bound
+    norm = None
+    ss = main_run["kernels"].get("sumsq")
+    if ss:
+        nbytes = w.batch * w.rows * w.cols * 2
+        norm = {"kernel": "sumsq_kernel (per-slice sum of squares)", "bytes_per_launch": nbytes,
+                "mean_launch_ms": ss["mean_ms"], "timed_launches": ss["launches"],
+                "achieved_GBps": nbytes / (ss["mean_ms"] * 1e-3) / 1e9, "peak_GBps": PEAK_HBM_GBS,
+                "frac": nbytes / (ss["mean_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
     cpu = None
     if args.cpu_budget > 0:
@@ -498,6 +512,7 @@ def main():
         "baseline_context": {"hardware": "1x H200", "ms_per_call": pages_ms,
                              "source": "prime-rl PR #3873, NS microbenchmark table (QuACK symmetric GEMM)"},
         "roofline": roof,
+        "norm_pass": norm,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
