@@ -169,9 +169,11 @@ int ns_query_last_config(char* buf, size_t n);
  * bit is set in `mask` (1 << NS_KIND_*) records two hipEvents in its own
  * dispatch packet (hipExtLaunchKernel: the kernel's start and end), so no
  * packet goes between the kernels of a call; 0 disables.  The events are
- * timing-only (no system-scope fence), so timed kernels run as they do
- * untimed; the stream must be synchronised before their results are read on
- * the host.
+ * timing-only (no system-scope fence); the stream must be synchronised
+ * before their results are read on the host.  A timed dispatch still
+ * releases its events at its end, which delays the next kernel by a few
+ * microseconds: time a sample of the launches (ns_timing_sample) where the
+ * call's own duration matters.
  * ns_timing_sample(every, offset): time only launch i of each kind (counted
  * from the last reset) with i % every == offset; every = 1, offset = 0 (the
  * default) times them all.  NS_ERR_INVALID_ARG unless 0 <= offset < every.
