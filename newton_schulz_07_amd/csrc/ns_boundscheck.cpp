@@ -350,7 +350,7 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
               if (mode == MODE_POLY) {
                 access(g.d_in, (db + j) * 4, 16, what);
                 access(g.d_in, (db + i) * 4, 4, what);
-                if (poly_reads_e) {
+                if (poly_reads_e && !(ti == tj && j > i)) {  // (not read: see the kernel)
                   const long long e0 = (long long)slice * g.e_bs + (long long)i * g.lde + j;
                   access(g.E, e0 * es, qsz, what);
                   // (a lower-triangle A: the element must be one the Gram stored)

@@ -596,10 +596,13 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
               }
             }
           } else if (MODE == MODE_POLY) {
-            float o[4];
+            float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             if constexpr (POLY_CAP)
               Quad<T>::unpack(obuf[a][b][rg], o);
-            else
+            else if (!(diag_tile && j > i))
+              // (a quad wholly above a diagonal tile's diagonal is replaced by
+              // the mirror of the lower half when stored: its O_A is not read,
+              // and with A stored as its lower block triangle it may not exist)
               Quad<T>::unpack(*reinterpret_cast<const QRaw*>(reinterpret_cast<const T*>(g.E) + (size_t)slice * g.e_bs +
                                                              (size_t)i * g.lde + j),
                               o);
