@@ -256,12 +256,13 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
       for (int b : {nat_p - 1, nat_p, nat_q - 1, nat_q})
         if (b > 0 && b < nk - 1) kst.push_back(b);
     }
-    // a diagonal Gram tile (2-slot ring) loads the P rows only, spread over
+    // a diagonal Gram or poly tile (2-slot ring) loads the P rows only, spread over
     // every wave, and reads its Q fragments from the P region: the operands
     // must be the same rows of the same matrix
-    const bool dshare = mode == MODE_GRAM && t.st == 2 && ti == tj;
+    const bool dshare = (mode == MODE_GRAM || mode == MODE_POLY) && t.st == 2 && ti == tj &&
+                        kind.p_nat == kind.q_nat && kind.p_sym == kind.q_sym;
     if (dshare && (g.P != g.Q || g.ldp != g.ldq || g.p_bs != g.q_bs || i0 != j0 || t.bm != t.bn || NIW % 2 ||
-                   kind.p_nat != kind.q_nat || NW * (NIW / 2) * 64 != t.bm * t.cpr))  // ... and cover every P chunk
+                   nat_p != nat_q || NW * (NIW / 2) * 64 != t.bm * t.cpr))  // ... and cover every P chunk
       fail(std::string(what) + ": diagonal tile shares operands that differ");
     for (int kt : kst)
       for (int wave = 0; wave < NW; ++wave)

@@ -255,19 +255,25 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
     src_off[t] = src_of(dma_src(idx, lane, BM, BN, CPR, EPC, PNAT, QNAT, ES), idx * 64 < LP ? PNAT : QNAT);
     if constexpr (HAS_SYM) src_alt[t] = src_of(dma_src(idx, lane, BM, BN, CPR, EPC, true, true, ES), true);
   }
-  // A diagonal Gram tile reads the same rows as P and as Q: its stages load
-  // the P rows only, spread over every wave, and its Q fragments are read
-  // from the P region.  (The 2-slot ring waits for all of a wave's loads at
-  // every stage, so a wave's load count may differ between tiles.)
-  constexpr bool DSH = MODE == MODE_GRAM && ST == 2;
+  // A diagonal Gram or poly tile reads the same rows as P and as Q (the
+  // Gram: rows or columns of X; the poly: rows of A): its stages load the P
+  // rows only, spread over every wave, and its Q fragments are read from the
+  // P region.  With A stored as its lower block triangle both operands switch
+  // layouts at the same stage (i0 == j0).  (The 2-slot ring waits for all of
+  // a wave's loads at every stage, so a wave's load count may differ between
+  // tiles.)
+  constexpr bool DSH = (MODE == MODE_GRAM || MODE == MODE_POLY) && ST == 2 && PL == QL;
+  constexpr bool DSH_SYM = DSH && PL == LAY_SYM;
   constexpr int NIP = NIW / 2;  // P loads per wave, spread over every wave
   static_assert(!DSH || (BM == BN && NIP * 2 == NIW), "diagonal sharing needs square tiles");
   const bool dshare = DSH && ti == tj;
-  unsigned src_dg[DSH ? NIP : 1];
+  unsigned src_dg[DSH ? NIP : 1], src_dga[DSH_SYM ? NIP : 1];
   if constexpr (DSH) {
 #pragma unroll
-    for (int t = 0; t < NIP; ++t)
+    for (int t = 0; t < NIP; ++t) {
       src_dg[t] = src_of(dma_src(wave * NIP + t, lane, BM, BN, CPR, EPC, PNAT, QNAT, ES), PNAT);
+      if constexpr (DSH_SYM) src_dga[t] = src_of(dma_src(wave * NIP + t, lane, BM, BN, CPR, EPC, true, true, ES), true);
+    }
   }
   const unsigned step_kc = (unsigned)(BK * ES);
   const unsigned step_np = (unsigned)(BK * g.ldp * ES), step_nq = (unsigned)(BK * g.ldq * ES);
@@ -288,9 +294,10 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
     if (DSH && dshare) {
 #pragma unroll
       for (int t = 0; t < (DSH ? NIP : 1); ++t) {
-        const int idx = wave * NIP + t;  // P chunks only
-        const unsigned off = src_dg[DSH ? t : 0] + (unsigned)kt * (PNAT ? step_np : step_kc);
-        const int kpos = dma_src(idx, lane, BM, BN, CPR, EPC, PNAT, QNAT, ES).kpos;
+        const int idx = wave * NIP + t;  // P chunks only, in this stage's layout (pn == qn here)
+        const unsigned base = (DSH_SYM && pn) ? src_dga[DSH_SYM ? t : 0] : src_dg[DSH ? t : 0];
+        const unsigned off = base + (unsigned)kt * (pn ? step_np : step_kc);
+        const int kpos = dma_src(idx, lane, BM, BN, CPR, EPC, pn, qn, ES).kpos;
         dma16(lds_addr(lds + slot * STAGE + idx * 64), (k0 + BK <= g.K || k0 + kpos < g.K) ? off : kOutOfRange, rP);
       }
     } else if (k0 + BK <= g.K) {
