@@ -200,7 +200,8 @@ int ns_timing_query(int kind, double* total_ms, int64_t* launches);
  * bytes (NaN in bf16 and in fp32) on its stream, so that any kernel reading
  * a workspace element that no earlier kernel of the call wrote turns the
  * result into NaN.  0 turns it off (the default).  For tests: it costs one
- * fill of the workspace per call.  Returns NS_OK.
+ * fill of the workspace per call, enqueued as a memset, so keep it off
+ * while a stream is being captured into a graph.  Returns NS_OK.
  */
 int ns_set_workspace_poison(int on);
 
