@@ -182,7 +182,7 @@ __device__ __forceinline__ int nat_lane_byte(int rb, int h, int lane, int rc, fl
 // LW loader waves join the WM x WN MFMA waves: they issue their share of the
 // K stages' loads and the stores, nothing else.
 template <typename T, int BM, int BN, int WM, int WN, int LW, int CPR, int ST, int OCC, int MODE, int PL, int QL,
-          int NG>
+          int NG, bool LATE>
 __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4) void gemm_kernel(
     const GemmLaunch<NG> L) {
   // operand layouts (OperandLayout): which read paths each operand needs
@@ -206,6 +206,7 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
   static_assert(CPR == 4 || CPR == 8 || CPR == 16, "4, 8 or 16 chunks per LDS row");
   static_assert(LP % 64 == 0 && STAGE % (64 * NW) == 0, "stage must split into whole wave loads");
   static_assert(ST >= 2 && NIW * (ST - 2) < 64, "ring depth");
+  static_assert(!LATE || (!mode_is_tri(MODE) && LW == 0), "late load issue: update tiles only");
 
   __shared__ uint4 lds[lds_chunks(BM, BN, CPR, ST, ES)];
 
@@ -388,7 +389,8 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
     }
   };
   // fragments of step s + 1 are read while the MFMAs of step s run
-  auto compute = [&](int slot, auto pn, auto qn) __attribute__((always_inline)) {
+  // `late` runs after the MFMAs of the first k step (the late load issue)
+  auto compute = [&](int slot, auto pn, auto qn, auto&& late) __attribute__((always_inline)) {
     uint4 pf[2][SM], qf[2][SN];
     load_step(slot, 0, pn, qn, pf[0], qf[0]);
 #pragma unroll
@@ -400,6 +402,11 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
       for (int a = 0; a < SM; ++a)
 #pragma unroll
         for (int b = 0; b < SN; ++b) mfma_chunk(acc[a][b], qf[s & 1][b], pf[s & 1][a], T());
+      if (LATE && s == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        late();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
   typedef std::integral_constant<bool, true> Nat;
@@ -527,9 +534,13 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
     else if (ST > 2 && after == 1) wait_vm_lgkm0<NIW>();
     else wait_vm_lgkm0<0>();
     ring_barrier();
-    if (kt + ST - 1 < nk) issue(kt + ST - 1, (u + ST - 1) % ST);
+    // the stage's loads go out here, or (LATE) after its first k step
+    auto late = [&]() __attribute__((always_inline)) {
+      if (LATE && kt + ST - 1 < nk) issue(kt + ST - 1, (u + ST - 1) % ST);
+    };
+    if (!LATE && kt + ST - 1 < nk) issue(kt + ST - 1, (u + ST - 1) % ST);
     if (!mw) return;
-    compute(u, pn, qn);
+    compute(u, pn, qn, late);
     // the poly's O_A capture happens at the stage covering the tile's own
     // columns, left of its diagonal, where P is K-contiguous
     if constexpr (MODE != MODE_GRAM && !(MODE == MODE_POLY && (decltype(pn)::value || !POLY_CAP))) capture(u, kt);
@@ -841,7 +852,7 @@ static void dispatch(K kernel, dim3 grid, dim3 block, hipStream_t st, A... args)
 // A launch over the groups gs[0 .. n): one group is a plain launch (NG = 1);
 // several go out kMaxLaunchGroups at a time, each launch's grid covering the
 // tiles of its groups.
-template <typename T, int MODE, int CLS, int PL, int QL>
+template <typename T, int MODE, int CLS, int PL, int QL, bool LATE = false>
 static hipError_t launch_mode(const GemmArgs* gs, int n, hipStream_t st) {
   constexpr TileCfg t = tile_cfg(std::is_same<T, bf16>::value ? 1 : 0, mode_is_tri(MODE), CLS);
   const dim3 block((t.wm * t.wn + t.lw) * 64);
@@ -849,7 +860,7 @@ static hipError_t launch_mode(const GemmArgs* gs, int n, hipStream_t st) {
     GemmLaunch<1> L{};
     L.g[0] = gs[0];
     L.n = 1;
-    dispatch(gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.lw, t.cpr, t.st, t.occ, MODE, PL, QL, 1>,
+    dispatch(gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.lw, t.cpr, t.st, t.occ, MODE, PL, QL, 1, LATE>,
              dim3(gs[0].tiles_per_slice * gs[0].batch), block, st, L);
     return hipGetLastError();
   }
@@ -861,7 +872,7 @@ static hipError_t launch_mode(const GemmArgs* gs, int n, hipStream_t st) {
         n - g0, [&](int i) { return (long long)gs[g0 + i].tiles_per_slice * gs[g0 + i].batch; }, L.start, &total);
     for (int i = 0; i < k; ++i) L.g[i] = gs[g0 + i];
     L.n = k;
-    dispatch(gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.lw, t.cpr, t.st, t.occ, MODE, PL, QL, kMaxLaunchGroups>,
+    dispatch(gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.lw, t.cpr, t.st, t.occ, MODE, PL, QL, kMaxLaunchGroups, LATE>,
              dim3((unsigned)total), block, st, L);
     if (hipError_t e = hipGetLastError()) return e;
     g0 += k;
@@ -879,8 +890,18 @@ static hipError_t launch_tri(int cls, const GemmArgs* gs, int n, hipStream_t st)
   }
 }
 
+// The late load issue of the update: bf16 launches of at most
+// kLateIssueMaxTiles tiles over all their groups.
+template <typename T>
+static bool late_issue_of(const GemmArgs* gs, int n) {
+  long long tiles = 0;
+  for (int i = 0; i < n; ++i) tiles += (long long)gs[i].tiles_per_slice * gs[i].batch;
+  return late_issue_tiles(std::is_same<T, bf16>::value ? 1 : 0, tiles);
+}
+
 template <typename T>
 static hipError_t dispatch_mode(const StageKind& k, const GemmArgs* gs, int n, hipStream_t st) {
+  auto late_issue = [](const GemmArgs* g, int m) { return late_issue_of<T>(g, m); };
   const bool wide = k.tri_cls == TRI_WIDE && std::is_same<T, bf16>::value;
   switch (k.mode) {
     case MODE_GRAM:
@@ -896,10 +917,12 @@ static hipError_t dispatch_mode(const StageKind& k, const GemmArgs* gs, int n, h
                   : launch_mode<T, MODE_POLY, TRI_NARROW, LAY_KCONT, LAY_KCONT>(gs, n, st);
     case MODE_UPD_ROW:
       if (k.p_sym || k.q_sym) return hipErrorInvalidValue;
-      return launch_mode<T, MODE_UPD_ROW, TRI_NARROW, LAY_KCONT, LAY_NAT>(gs, n, st);
+      return late_issue(gs, n) ? launch_mode<T, MODE_UPD_ROW, TRI_NARROW, LAY_KCONT, LAY_NAT, true>(gs, n, st)
+                               : launch_mode<T, MODE_UPD_ROW, TRI_NARROW, LAY_KCONT, LAY_NAT>(gs, n, st);
     case MODE_UPD_COL:
       if (k.p_sym || k.q_sym) return hipErrorInvalidValue;
-      return launch_mode<T, MODE_UPD_COL, TRI_NARROW, LAY_KCONT, LAY_KCONT>(gs, n, st);
+      return late_issue(gs, n) ? launch_mode<T, MODE_UPD_COL, TRI_NARROW, LAY_KCONT, LAY_KCONT, true>(gs, n, st)
+                               : launch_mode<T, MODE_UPD_COL, TRI_NARROW, LAY_KCONT, LAY_KCONT>(gs, n, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -249,6 +249,14 @@ inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* 
   return poly_args(p, choose_tiles(p), oa, da, oc, dc, a, b, c, kind);
 }
 
+// Update launches of at most this many tiles (four rounds on 256 CUs) issue
+// each stage's operand loads after the stage's first k step rather than
+// before it: their MFMA work, not their loads, sets their pace, and the
+// loads then leave the MFMAs' start alone.  Launches with more tiles wait on
+// their loads and keep the early issue.
+constexpr long long kLateIssueMaxTiles = 1024;
+inline bool late_issue_tiles(int dtype, long long tiles) { return dtype == 1 && tiles <= kLateIssueMaxTiles; }
+
 // X' = C X (rows <= cols) or X C (rows > cols), C = O_C + diag(d_C).
 inline GemmArgs update_args(const Plan& p, const void* x, const void* oc, const float* dc, void* xo,
                             StageKind* kind, const float* d_norm = nullptr) {
