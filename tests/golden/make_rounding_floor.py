@@ -38,7 +38,9 @@ def rel(a, b):
 def main(names):
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "rounding_floor.json")
     out = {"what": "relative Frobenius error vs the fp64 oracle of the CPU bf16 rounding model "
-                   "(oracle/rounding_model.py); 'diag' is the placement the HIP kernels use",
+                   "(oracle/rounding_model.py). 'shipped': the diagonal split with the normalisation "
+                   "folded into the first step (X0 never rounded), the placement the HIP kernels use; "
+                   "'literal': bf16 A, B and X with a stored bf16 X0, the plain reading",
            "workloads": {}}
     if names:
         with open(path) as f:
@@ -52,9 +54,9 @@ def main(names):
         for i in SAMPLES.get(name, [0]):
             xi = xs[i]
             ref = newton_schulz(xi.double().numpy())          # oracle reads the given tensor
-            xb = xi.to(torch.bfloat16).float().numpy()         # the bf16 path's input
-            rec[str(i)] = {"diag": rel(ns_bf16_model(xb, placement="diag"), ref),
-                           "plain": rel(ns_bf16_model(xb, placement="plain"), ref)}
+            xb = xi.to(torch.bfloat16).double().numpy()         # the bf16 path's input
+            rec[str(i)] = {"shipped": rel(ns_bf16_model(xb), ref),
+                           "literal": rel(ns_bf16_model(xb, placement="literal", fold_norm=False), ref)}
         out["workloads"][name] = rec
         print(name, rec, f"{time.time() - t0:.0f}s", flush=True)
     # the transposed MLP weight has the same floor (NS(Xᵀ) = NS(X)ᵀ)

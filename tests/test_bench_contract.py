@@ -52,3 +52,4 @@ def test_short_run_prints_one_complete_line():
     assert d["measured_peak"]["tflops"] > 0 and d["measured_peak"]["shader_clock_mhz"] > 0
     assert d["norm_pass"] is not None and 0.0 < d["norm_pass"]["frac"] < 1.0
     assert d["cpu_baseline"] is None  # --cpu-budget 0
+    assert d["vs_baseline"] is None  # the pages' H200 figure is context only

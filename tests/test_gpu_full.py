@@ -1,17 +1,20 @@
 """Full-size parity: every named workload at its real shape, in the launch
 configuration the benchmark times (the whole stack in one call), against the
-fp64 oracle on sampled slices (the oracle computes slices one by one).
+fp64 oracle on every slice (the oracle computes slices one by one).
 
 Bars (relative Frobenius error per slice):
-  * bf16 path: <= 1e-2.  Two workloads cannot meet it with ANY bf16 iterate:
-    on the rank-64-plus-noise square and the rank-32-plus-noise MLP weight the
-    low-rank part dominates every entry, so rounding X to bf16 perturbs the
-    noise subspace by about the noise itself, and NS amplifies small singular
-    values (about a^5 ≈ 485).  The CPU rounding model
-    (tests/golden/rounding_floor.json) puts their floor above 1e-2.  For those
-    the bar is 1.25 x that floor, and a strict xfail records the 1e-2 miss.
-  * fp32 path on the same inputs: <= 1e-3 (fp32 vs fp64 NS differ by a few
-    1e-4 at these sizes), which checks every tile of the kernels at full size.
+  * bf16 path: <= 1e-2, and on the slices the CPU rounding model covers
+    (tests/golden/rounding_floor.json, 'shipped': the placement the library
+    uses) <= 1.1 x the model's error.  Two workloads cannot meet 1e-2 with ANY
+    bf16 iterate: on the rank-64-plus-noise square and the rank-32-plus-noise
+    MLP weight the low-rank part dominates every entry, so rounding X to bf16
+    perturbs the noise subspace by about the noise itself, and NS amplifies
+    small singular values (about a^5 ≈ 485).  The model puts their floor above
+    1e-2; for those only the 1.1 x model bar applies, and a strict xfail
+    records the 1e-2 miss.  The kernels are bitwise deterministic, so these
+    numbers do not move from run to run.
+  * fp32 path on the same inputs: <= 1e-4, which checks every tile of the
+    kernels at full size.
 """
 
 import json
@@ -29,8 +32,6 @@ from tests.gpu_util import device, rel_err, report, to64
 pytestmark = pytest.mark.gpu
 
 FLOOR = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "rounding_floor.json")))["workloads"]
-SAMPLES = {"experts16_1536x2048": [0, 7, 15], "experts128_1536x2048": [0, 63, 127],
-           "experts32_7168x2048": [0, 31], "experts128_2048x768": [0, 64, 127]}
 FLOORED = {"lowrank64_4096x4096", "mlp_4096x14336", "mlp_14336x4096"}
 
 _oracle_cache = {}
@@ -47,18 +48,19 @@ def oracle_slice(name, x, i):
 
 
 def run(name, dtype):
+    """One whole-stack call; the error of every slice against the oracle."""
     w = WORKLOADS[name]
     x = make_workload(name)
     xg = x.to(dtype).to(device())
     y = ns.orthogonalize(xg)
     torch.cuda.synchronize()
-    xs = x.reshape(-1, w.rows, w.cols)
-    ys = y.reshape(-1, w.rows, w.cols)
-    errs = {}
-    for i in SAMPLES.get(name, [0]):
-        ref = oracle_slice(name, xs[i], i)
-        errs[i] = float(rel_err(to64(ys[i]), ref)[0])
     assert torch.isfinite(y).all()
+    xs = x.reshape(-1, w.rows, w.cols)
+    ys = y.reshape(-1, w.rows, w.cols).cpu()
+    del xg, y
+    errs = {}
+    for i in range(w.batch):
+        errs[i] = float(rel_err(to64(ys[i]), oracle_slice(name, xs[i], i))[0])
     return errs
 
 
@@ -66,15 +68,20 @@ NAMES = ["lowrank64_4096x4096", "mlp_4096x14336", "mlp_14336x4096", "experts16_1
          "experts128_1536x2048", "experts32_7168x2048", "square_8192x8192", "experts128_2048x768"]
 
 
+def summary(errs):
+    v = np.array(list(errs.values()))
+    return {"slices": len(v), "max": float(v.max()), "mean": float(v.mean()), "argmax": int(v.argmax())}
+
+
 @pytest.mark.parametrize("name", NAMES)
 def test_full_size_bf16(name):
     errs = run(name, torch.bfloat16)
-    floors = {int(k): v["diag"] for k, v in FLOOR[name].items()}
-    report({"case": f"full_bf16_{name}", "errs": errs, "model_floor": floors})
+    floors = {int(k): v["shipped"] for k, v in FLOOR[name].items()}
+    report({"case": f"full_bf16_{name}", **summary(errs), "model_floor": floors})
     for i, e in errs.items():
-        if name in FLOORED:
-            assert e <= 1.25 * floors[i], (i, e, floors[i])
-        else:
+        if i in floors:
+            assert e <= 1.1 * floors[i], (i, e, floors[i])
+        if name not in FLOORED:
             assert e <= 1e-2, (i, e)
 
 
@@ -86,12 +93,26 @@ def test_full_size_bf16_meets_1e_2_on_floored_inputs(name):
     assert max(errs.values()) <= 1e-2
 
 
-@pytest.mark.parametrize("name", ["lowrank64_4096x4096", "mlp_14336x4096", "experts16_1536x2048",
-                                  "experts32_7168x2048"])
+@pytest.mark.parametrize("name", NAMES)
 def test_full_size_fp32(name):
     errs = run(name, torch.float32)
-    report({"case": f"full_fp32_{name}", "errs": errs})
-    assert max(errs.values()) <= 1e-3
+    report({"case": f"full_fp32_{name}", **summary(errs)})
+    assert max(errs.values()) <= 1e-4
+
+
+@pytest.mark.parametrize("name,slices", [("experts128_1536x2048", (0, 63, 127)),
+                                         ("experts128_2048x768", (0, 64, 127)),
+                                         ("experts32_7168x2048", (0, 31))])
+def test_full_size_batch_invariance(name, slices):
+    # slice i of the whole-stack call (lower-block-triangle A, stack tile
+    # classes, XCD-remapped grid) equals the single-slice call bitwise
+    w = WORKLOADS[name]
+    xg = make_workload(name).to(device())
+    y = ns.orthogonalize(xg)
+    for i in slices:
+        yi = ns.orthogonalize(xg[i:i + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(yi[0], y[i]), f"slice {i} of {w.shape} differs from its single-slice call"
 
 
 @pytest.mark.parametrize("name", ["iid_256x512", "lowrank64_4096x4096", "experts16_1536x2048",
@@ -110,9 +131,10 @@ def test_bf16_at_least_as_accurate_as_dense_bf16(name):
     xs = x.reshape(-1, w.rows, w.cols)
     ys, yds = y.reshape(-1, w.rows, w.cols), yd.reshape(-1, w.rows, w.cols)
     errs = {}
-    for i in SAMPLES.get(name, [0]):
+    for i in range(w.batch):
         ref = oracle_slice(name, xs[i], i)
         errs[i] = (float(rel_err(to64(ys[i]), ref)[0]), float(rel_err(to64(yds[i]), ref)[0]))
-    report({"case": f"vs_dense_{name}", "errs_ours_dense": errs})
+    report({"case": f"vs_dense_{name}", "max_ours": max(e for e, _ in errs.values()),
+            "max_dense": max(d for _, d in errs.values())})
     for i, (e, ed) in errs.items():
         assert e <= ed, (i, e, ed)

@@ -183,13 +183,14 @@ def test_dims_not_multiple_of_8(shape):
     torch.cuda.synchronize()
     assert y32.shape == x.shape and yb.shape == x.shape
     assert rel_err(to64(y32), ref).max() <= 1e-4
-    # bf16: 1e-2, or 1.25 x the CPU rounding model's floor where a tiny slice
-    # puts that floor above 1e-2 (slice 0 of 3x9x13: 1.12e-2)
-    floor = np.array([rel_err(ns_bf16_model(x[i].to(torch.bfloat16).float().numpy(), placement="diag"),
+    # bf16: 1e-2, or 1.1 x the CPU rounding model's floor (the library's
+    # placement) where a tiny slice puts that floor above 1e-2 (slice 0 of
+    # 3x9x13: 1.03e-2)
+    floor = np.array([rel_err(ns_bf16_model(x[i].to(torch.bfloat16).double().numpy()),
                               ref[i])[0] for i in range(shape[0])])
     e = rel_err(to64(yb), ref)
     report({"case": f"odd_bf16_{shape}", "errs": e.tolist(), "model_floor": floor.tolist()})
-    assert np.all(e <= np.maximum(1e-2, 1.25 * floor)), (e, floor)
+    assert np.all(e <= np.maximum(1e-2, 1.1 * floor)), (e, floor)
     assert "zero-padded" in ns.ns_query_last_config()
 
 
