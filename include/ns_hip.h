@@ -97,7 +97,14 @@ enum {
  * A is mirrored too, except on large bf16 stacks, where it is kept as its
  * lower block triangle and the polynomial reads the rest transposed.
  * The workspace (ns_workspace_bytes) is allocated on first use per
- * (device, stream) and grown when needed; growing synchronises the device.
+ * (device, stream) and grown when needed.  Growing allocates a new buffer
+ * without synchronising; the replaced one stays allocated (work queued
+ * earlier may still use it) until ns_release_workspace.  Once the workspace
+ * of (device, stream) is at least this call's size, a call makes no
+ * allocation and no synchronisation: it enqueues only kernels (and, in place
+ * with an odd step count, one device copy), so it can be captured into a
+ * HIP graph, provided the capture runs on that same stream and workspace
+ * poisoning is off.
  */
 int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows,
                      int64_t cols, int dtype, int ns_steps, float a, float b,
@@ -146,9 +153,14 @@ size_t ns_workspace_bytes_grouped(int n_groups, const int64_t* batch,
                                   const int64_t* rows, const int64_t* cols,
                                   int dtype);
 
-/* Free every cached workspace (all devices and streams).  Synchronises each
- * device that held one.  Returns NS_OK or NS_ERR_HIP. */
+/* Free every cached workspace (all devices and streams), replaced ones
+ * included.  Synchronises each device that held one.  Must not run while
+ * another thread is inside a call.  Returns NS_OK or NS_ERR_HIP. */
 int ns_release_workspace(void);
+
+/* Number of workspace allocations (hipMalloc) the library has made since it
+ * was loaded.  A call whose workspace is warm leaves it unchanged. */
+int64_t ns_workspace_allocations(void);
 
 /* ---- diagnostics --------------------------------------------------------- */
 

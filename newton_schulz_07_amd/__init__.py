@@ -33,6 +33,7 @@ SIGNATURES = {
     "ns_orthogonalize_grouped": (_int, [_int, _pvp, _pvp, _pi64, _pi64, _pi64, _int, _int, _flt, _flt, _flt, _vp]),
     "ns_workspace_bytes_grouped": (_sz, [_int, _pi64, _pi64, _pi64, _int]),
     "ns_release_workspace": (_int, []),
+    "ns_workspace_allocations": (_i64, []),
     "ns_status_string": (ctypes.c_char_p, [_int]),
     "ns_last_error": (ctypes.c_char_p, []),
     "ns_query_last_config": (_int, [ctypes.c_char_p, _sz]),
@@ -192,6 +193,11 @@ def ns_workspace_bytes(batch, rows, cols, dtype_code):
 
 def ns_release_workspace():
     _check(lib().ns_release_workspace())
+
+
+def ns_workspace_allocations():
+    """Workspace allocations the library has made since it was loaded."""
+    return int(lib().ns_workspace_allocations())
 
 
 def ns_query_last_config():

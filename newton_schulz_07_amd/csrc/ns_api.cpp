@@ -100,25 +100,29 @@ struct Ws {
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, void*>, Ws> g_ws;
+// Buffers replaced by a larger one.  Work queued earlier may still read
+// them, and another thread may hold the pointer between taking it and
+// enqueueing its launches, so they are freed only by ns_release_workspace.
+std::vector<std::pair<int, void*>> g_ws_retired;
+std::atomic<int64_t> g_ws_allocs{0};
 
+// The workspace of (current device, st), grown to at least `bytes`.  A warm
+// workspace is returned without any HIP call, so calls on a stream that has
+// seen a call of the same or a larger size enqueue only kernels and copies
+// (graph capture needs exactly that).
 int get_workspace(hipStream_t st, size_t bytes, char** out) {
   int dev = 0;
   if (int s = check_hip(hipGetDevice(&dev), "hipGetDevice")) return s;
   std::lock_guard<std::mutex> lk(g_ws_mu);
   Ws& w = g_ws[{dev, (void*)st}];
   if (w.bytes < bytes) {
-    if (w.ptr != nullptr) {
-      // the old buffer may still be read by work queued earlier
-      if (int s = check_hip(hipDeviceSynchronize(), "hipDeviceSynchronize")) return s;
-      if (int s = check_hip(hipFree(w.ptr), "hipFree")) return s;
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
     void* p = nullptr;
     if (hipMalloc(&p, bytes) != hipSuccess || p == nullptr) {
       (void)hipGetLastError();
       return fail(NS_ERR_OOM, "workspace allocation of " + std::to_string(bytes) + " bytes failed");
     }
+    ++g_ws_allocs;
+    if (w.ptr != nullptr) g_ws_retired.emplace_back(dev, w.ptr);
     w.ptr = p;
     w.bytes = bytes;
   }
@@ -536,17 +540,28 @@ int ns_release_workspace(void) {
   int status = NS_OK;
   int cur = 0;
   (void)hipGetDevice(&cur);
-  for (auto& kv : g_ws) {
-    if (kv.second.ptr == nullptr) continue;
-    if (hipSetDevice(kv.first.first) == hipSuccess) {
-      (void)hipDeviceSynchronize();
-      if (hipFree(kv.second.ptr) != hipSuccess) status = fail(NS_ERR_HIP, "hipFree failed");
+  std::vector<std::pair<int, void*>> bufs = g_ws_retired;
+  for (auto& kv : g_ws)
+    if (kv.second.ptr != nullptr) bufs.emplace_back(kv.first.first, kv.second.ptr);
+  std::map<int, bool> synced;
+  for (auto& db : bufs) {
+    if (hipSetDevice(db.first) != hipSuccess) {
+      status = fail(NS_ERR_HIP, "hipSetDevice failed");
+      continue;
     }
+    if (!synced[db.first]) {
+      (void)hipDeviceSynchronize();
+      synced[db.first] = true;
+    }
+    if (hipFree(db.second) != hipSuccess) status = fail(NS_ERR_HIP, "hipFree failed");
   }
   g_ws.clear();
+  g_ws_retired.clear();
   (void)hipSetDevice(cur);
   return status;
 }
+
+int64_t ns_workspace_allocations(void) { return g_ws_allocs.load(); }
 
 const char* ns_status_string(int status) {
   switch (status) {
