@@ -59,8 +59,10 @@ typedef enum {
                              exports also rows or cols not a multiple of 8 */
   NS_ERR_ARCH = 4,        /* current device is not gfx950                 */
   NS_ERR_OOM = 5,         /* workspace allocation failed                  */
-  NS_ERR_HIP = 6          /* a HIP runtime call or launch failed;
+  NS_ERR_HIP = 6,         /* a HIP runtime call or launch failed;
                              details in ns_last_error()                   */
+  NS_ERR_SCRATCH = 7      /* ns_orthogonalize_noalloc: the call needs more
+                             than NS_NOALLOC_SCRATCH_BYTES of workspace    */
 } ns_status;
 
 /* Storage and compute dtype of every matrix of one call. */
@@ -112,6 +114,35 @@ int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows,
 
 /* Bytes of library workspace one ns_orthogonalize call of this shape needs. */
 size_t ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int dtype);
+
+/*
+ * ns_orthogonalize_noalloc - ns_orthogonalize for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * Same arguments, checks, kernels and results as ns_orthogonalize (bitwise),
+ * but the workspace is a fixed device array inside the library, one copy
+ * per GPU, of NS_NOALLOC_SCRATCH_BYTES (256 MiB), held from the moment the
+ * library's code is loaded on that GPU until the process ends.  The call
+ * makes no device allocation (no hipMalloc, no hipFree, no allocating
+ * library routine) and no synchronisation; the caller still provides in and
+ * out.  A shape whose ns_workspace_bytes() exceeds NS_NOALLOC_SCRATCH_BYTES
+ * is rejected with NS_ERR_SCRATCH before anything is enqueued (256 MiB
+ * covers, e.g., bf16 4096 x 4096, 4096 x 14336 and 16 x 1536 x 2048).
+ *
+ * Every call on a GPU uses that GPU's one array and leaves its last contents
+ * there; nothing in it has to start at zero (every kernel writes what a later
+ * one reads).  Calls that overlap in time on one GPU - on different streams,
+ * or from different threads without ordering - race on the array; order
+ * them on one stream.  Kernel timing (ns_timing_*) does not apply to this
+ * entry point.  Workspace poisoning (ns_set_workspace_poison) does, with
+ * a memset of the array.
+ */
+#define NS_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int ns_orthogonalize_noalloc(const void* in, void* out, int64_t batch,
+                             int64_t rows, int64_t cols, int dtype,
+                             int ns_steps, float a, float b, float c,
+                             void* stream);
 
 /*
  * ns_orthogonalize_grouped - the same method on several stacks of different

@@ -30,6 +30,7 @@ NS_MAX_GROUPS = 4096
 SIGNATURES = {
     "ns_orthogonalize": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _flt, _flt, _flt, _vp]),
     "ns_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
+    "ns_orthogonalize_noalloc": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _flt, _flt, _flt, _vp]),
     "ns_orthogonalize_grouped": (_int, [_int, _pvp, _pvp, _pi64, _pi64, _pi64, _int, _int, _flt, _flt, _flt, _vp]),
     "ns_workspace_bytes_grouped": (_sz, [_int, _pi64, _pi64, _pi64, _int]),
     "ns_release_workspace": (_int, []),
@@ -128,6 +129,27 @@ def ns_orthogonalize(x, out=None, ns_steps=DEFAULT_STEPS, a=DEFAULT_COEFFS[0], b
     with torch.cuda.device(x.device):
         _check(lib().ns_orthogonalize(_ptr(x), _ptr(out), batch, rows, cols, _dtype_code(x),
                                       int(ns_steps), float(a), float(b), float(c), _stream(x)))
+    return out
+
+
+NS_NOALLOC_SCRATCH_BYTES = 256 << 20
+
+
+def ns_orthogonalize_noalloc(x, out, ns_steps=DEFAULT_STEPS, a=DEFAULT_COEFFS[0], b=DEFAULT_COEFFS[1],
+                             c=DEFAULT_COEFFS[2]):
+    """ns_orthogonalize on the library's fixed device scratch: no device
+    allocation by the library (out must be given; the binding allocates
+    nothing either).  Shapes needing more than NS_NOALLOC_SCRATCH_BYTES of
+    workspace raise NSError (NS_ERR_SCRATCH)."""
+    _need_gpu_tensor(x, "x")
+    _need_gpu_tensor(out, "out")
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    batch, rows, cols = _brc(x)
+    import torch
+    with torch.cuda.device(x.device):
+        _check(lib().ns_orthogonalize_noalloc(_ptr(x), _ptr(out), batch, rows, cols, _dtype_code(x),
+                                              int(ns_steps), float(a), float(b), float(c), _stream(x)))
     return out
 
 

@@ -29,7 +29,7 @@ HIP_FLAGS = [
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,
 ]
-SOURCES = ["ns_kernels.hip", "ns_peak.hip", "ns_api.cpp"]
+SOURCES = ["ns_kernels.hip", "ns_peak.hip", "ns_noalloc.hip", "ns_api.cpp"]
 
 
 def hipcc():

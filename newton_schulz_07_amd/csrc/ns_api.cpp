@@ -159,10 +159,15 @@ hipEvent_t take_event() {
   return e;
 }
 
+// Set while the allocation-free entry point enqueues: its launches are
+// neither timed nor counted (timing may create events).
+thread_local bool t_untimed = false;
+
 // The events travel in the kernel's dispatch packet (ns::set_launch_events),
 // so timing adds no packets between the kernels of a call.
 template <typename F>
 hipError_t timed_launch(int kind, hipStream_t st, F&& f) {
+  if (t_untimed) return f();
   std::unique_lock<std::mutex> lk(g_t_mu);
   const bool on = ((g_t_mask >> kind) & 1) && g_t_count[kind]++ % g_t_every == g_t_offset;
   hipEvent_t a = nullptr, b = nullptr;
@@ -337,11 +342,15 @@ int check_grouped(int n, const void* const* in, void* const* out, const int64_t*
 // (Gram, poly, update launches of one step) describe what ran.
 std::atomic<int> g_poison{0};  // ns_set_workspace_poison
 
+//
+// The workspace is the library's cache for (device, st), or `given` (at
+// least ws_bytes) when that is not null.
 int run_stacks(std::vector<Group>& gs, size_t ws_bytes, int ns_steps, float a, float b, float c, hipStream_t st,
-               ns::TileChoice* tc, int launches[3]) {
+               ns::TileChoice* tc, int launches[3], char* given = nullptr) {
   const int dtype = gs[0].p.dtype;
-  char* ws = nullptr;
-  if (int s = get_workspace(st, ws_bytes, &ws)) return s;
+  char* ws = given;
+  if (ws == nullptr)
+    if (int s = get_workspace(st, ws_bytes, &ws)) return s;
   if (g_poison.load() && ws_bytes > 0)
     if (int s = check_hip(hipMemsetAsync(ws, 0xFF, ws_bytes, st), "workspace poison fill")) return s;
   std::vector<Plan> plans;
@@ -496,6 +505,42 @@ int ns_orthogonalize(const void* in, void* out, int64_t batch, int64_t rows, int
   return NS_OK;
 }
 
+int ns_orthogonalize_noalloc(const void* in, void* out, int64_t batch, int64_t rows, int64_t cols, int dtype,
+                             int ns_steps, float a, float b, float c, void* stream) {
+  t_err.clear();
+  if (int s = common_checks(batch, rows, cols, dtype, true)) return s;
+  if (ns_steps < 0) return fail(NS_ERR_INVALID_ARG, "ns_steps must be >= 0");
+  if (int s = check_ptr(in, "in")) return s;
+  if (int s = check_ptr(out, "out")) return s;
+  const size_t bytes = (size_t)batch * rows * cols * esize(dtype);
+  if (in != out && overlaps(in, bytes, out, bytes))
+    return fail(NS_ERR_INVALID_ARG, "out overlaps in without being the same pointer");
+  if (batch == 0) return NS_OK;
+  std::vector<Group> gs(1);
+  gs[0].p = make_plan(batch, rows, cols, dtype);
+  if (gs[0].p.total > NS_NOALLOC_SCRATCH_BYTES)
+    return fail(NS_ERR_SCRATCH, "this call needs " + std::to_string(gs[0].p.total) +
+                                    " bytes of workspace, more than the fixed scratch of " +
+                                    std::to_string(NS_NOALLOC_SCRATCH_BYTES) + " bytes");
+  if (int s = check_arch()) return s;
+  int dev = 0;
+  if (int s = check_hip(hipGetDevice(&dev), "hipGetDevice")) return s;
+  char* ws = nullptr;
+  if (int s = check_hip(ns::noalloc_scratch(dev, &ws), "scratch address (hipGetSymbolAddress)")) return s;
+  gs[0].ws_off = 0;
+  gs[0].uin = in;
+  gs[0].uout = out;
+  ns::TileChoice tc;
+  int launches[3];
+  t_untimed = true;
+  const int s = run_stacks(gs, gs[0].p.total, ns_steps, a, b, c, static_cast<hipStream_t>(stream), &tc, launches, ws);
+  t_untimed = false;
+  if (s) return s;
+  record_config(gs[0].p, ns_steps);
+  t_cfg += " | workspace: fixed scratch";
+  return NS_OK;
+}
+
 int ns_orthogonalize_grouped(int n_groups, const void* const* in, void* const* out, const int64_t* batch,
                              const int64_t* rows, const int64_t* cols, int dtype, int ns_steps, float a, float b,
                              float c, void* stream) {
@@ -572,6 +617,7 @@ const char* ns_status_string(int status) {
     case NS_ERR_ARCH: return "NS_ERR_ARCH: device is not gfx950";
     case NS_ERR_OOM: return "NS_ERR_OOM: workspace allocation failed";
     case NS_ERR_HIP: return "NS_ERR_HIP: HIP runtime error";
+    case NS_ERR_SCRATCH: return "NS_ERR_SCRATCH: the call needs more than the fixed no-alloc scratch";
     default: return "unknown status";
   }
 }

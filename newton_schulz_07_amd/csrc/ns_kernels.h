@@ -22,6 +22,11 @@ hipError_t launch_sumsq_grouped(int dtype, const NormArgs* gs, const int* batch,
 hipError_t launch_scale(int dtype, const NormArgs& g, int batch, hipStream_t st);
 hipError_t launch_pad(int dtype, const PadArgs& g, hipStream_t st);
 
+// Device address of the fixed scratch array (ns_noalloc.hip) on device
+// `dev`, which must be the current device.  The first call per device takes
+// it with hipGetSymbolAddress; later calls return the kept value.
+hipError_t noalloc_scratch(int dev, char** ptr);
+
 // matrix-core calibration loop (ns_peak.hip): `blocks` workgroups of
 // kPeakThreads threads, each wave `iters` (a multiple of 4) rounds of
 // mfma_peak_acc() MFMAs; sink takes one float per thread, clocks four

@@ -218,3 +218,23 @@ def test_grouped_launch_indexes_stay_in_bounds(boundscheck, case):
     r = subprocess.run([boundscheck, "--group"] + case.split(), capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "violations=0" in r.stdout
+
+
+def test_noalloc_rejects_bad_arguments_and_oversized_calls_before_any_launch():
+    L = ns.lib()
+
+    def noalloc(batch=1, rows=256, cols=512, dtype=1, steps=5, inp=FAKE_IN, out=FAKE_OUT):
+        return L.ns_orthogonalize_noalloc(ctypes.c_void_p(inp), ctypes.c_void_p(out), batch, rows, cols, dtype,
+                                          steps, 3.4445, -4.775, 2.0315, None)
+    assert noalloc(inp=0) == 1
+    assert noalloc(steps=-1) == 1
+    assert noalloc(dtype=3) == 2
+    assert noalloc(out=FAKE_OUT + 4) == 3
+    assert noalloc(batch=0) == 0  # nothing to do, nothing touched
+    # the fixed scratch is 256 MiB: 8192^2 bf16 needs 384 MiB, 128 x 1536 x 2048 about 1.9 GiB
+    for shape in ((1, 8192, 8192), (128, 1536, 2048)):
+        assert ns.ns_workspace_bytes(*shape, 1) > ns.NS_NOALLOC_SCRATCH_BYTES
+        assert noalloc(*shape, out=FAKE_IN + 0x100000000) == 7  # out past the end of in
+        assert "fixed scratch" in L.ns_last_error().decode()
+    assert L.ns_status_string(7).decode().startswith("NS_ERR_SCRATCH")
+    assert ns.ns_workspace_bytes(1, 4096, 4096, 1) <= ns.NS_NOALLOC_SCRATCH_BYTES
