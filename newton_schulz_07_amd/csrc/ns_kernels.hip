@@ -34,6 +34,8 @@
 #define NS_FRAG_BARRIER 1
 #endif
 
+
+
 namespace ns {
 
 typedef __bf16 bf16;
@@ -388,8 +390,25 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
       else qf[b] = *reinterpret_cast<const uint4*>(st + kcq[Q_KC ? (s ^ kc_sigma(b, CPR)) : 0] + b * 32 * CPR * 16);
     }
   };
+  // The k step after whose MFMAs a wave issues its share of the next
+  // stage's loads (-1: at the stage's barrier).  A wave that issues them is
+  // held up while its CU's vector-memory path accepts them (about 500
+  // cycles when all 8 waves issue 8 KB each at once), so in the bf16
+  // update's launches of more than four rounds, and in the 256 x 256 Gram,
+  // the waves of tile row half 1 issue one k step after those of half 0:
+  // the two waves of a SIMD then take turns, one issuing loads while the
+  // other keeps the matrix core busy.  With fewer than 16 K stages the
+  // later half of each stage's loads lands too late, and update launches of
+  // up to four rounds issue every wave's loads after the first k step
+  // (LATE).  (The 128 x 128 triangle tiles, two workgroups per CU, lose
+  // from it: their lower-triangle poly then spills.)
+  constexpr bool STAGGER = (MODE == MODE_UPD_ROW || MODE == MODE_UPD_COL || (mode_is_tri(MODE) && BM == 256)) &&
+                           ST == 2 && LW == 0 && std::is_same<T, bf16>::value;
+  const int issue_step = !STAGGER ? -1
+                         : LATE   ? 0
+                                  : (wm == 1 && (g.K + BK - 1) / BK >= kStaggerMinStages ? 0 : -1);
   // fragments of step s + 1 are read while the MFMAs of step s run
-  // `late` runs after the MFMAs of the first k step (the late load issue)
+  // `late` issues the next stage's loads after the MFMAs of k step issue_step
   auto compute = [&](int slot, auto pn, auto qn, auto&& late) __attribute__((always_inline)) {
     uint4 pf[2][SM], qf[2][SN];
     load_step(slot, 0, pn, qn, pf[0], qf[0]);
@@ -402,7 +421,7 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
       for (int a = 0; a < SM; ++a)
 #pragma unroll
         for (int b = 0; b < SN; ++b) mfma_chunk(acc[a][b], qf[s & 1][b], pf[s & 1][a], T());
-      if (LATE && s == 0) {
+      if (STAGGER && s == issue_step) {
         __builtin_amdgcn_sched_barrier(0);
         late();
         __builtin_amdgcn_sched_barrier(0);
@@ -534,11 +553,11 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
     else if (ST > 2 && after == 1) wait_vm_lgkm0<NIW>();
     else wait_vm_lgkm0<0>();
     ring_barrier();
-    // the stage's loads go out here, or (LATE) after its first k step
+    // the stage's loads go out here, or after the k step issue_step
     auto late = [&]() __attribute__((always_inline)) {
-      if (LATE && kt + ST - 1 < nk) issue(kt + ST - 1, (u + ST - 1) % ST);
+      if (kt + ST - 1 < nk) issue(kt + ST - 1, (u + ST - 1) % ST);
     };
-    if (!LATE && kt + ST - 1 < nk) issue(kt + ST - 1, (u + ST - 1) % ST);
+    if (issue_step < 0) late();
     if (!mw) return;
     compute(u, pn, qn, late);
     // the poly's O_A capture happens at the stage covering the tile's own

@@ -255,6 +255,9 @@ inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* 
 // loads then leave the MFMAs' start alone.  Launches with more tiles wait on
 // their loads and keep the early issue.
 constexpr long long kLateIssueMaxTiles = 1024;
+// Larger bf16 update launches with at least this many K stages stagger the
+// load issue of the two tile-row halves by one k step (see the kernel).
+constexpr int kStaggerMinStages = 16;
 inline bool late_issue_tiles(int dtype, long long tiles) { return dtype == 1 && tiles <= kLateIssueMaxTiles; }
 
 // X' = C X (rows <= cols) or X C (rows > cols), C = O_C + diag(d_C).
