@@ -85,11 +85,26 @@ NS_HD constexpr long long tri_tiles(long long batch, long long m, int tile) {
 // quads of the whole wave tile in registers.  t128 / t256: the launch's
 // triangle tiles at 128 and at 256 (summed over every stack it covers).
 enum TriClass { TRI_NARROW = 0, TRI_WIDE = 1, TRI_BIG = 2 };
-NS_HD constexpr int tri_class_of_tiles(int dtype, long long t128, long long t256, bool gram) {
-  return (dtype == 1 && t128 < 1024) ? TRI_WIDE : (gram && dtype == 1 && t256 >= 1024) ? TRI_BIG : TRI_NARROW;
+// Rounds of a launch of `tiles` workgroups over `slots` resident ones.
+NS_HD constexpr long long launch_rounds(long long tiles, long long slots) { return (tiles + slots - 1) / slots; }
+// A launch whose stacks all have m >= 4096 (so K >= 4096 for both products)
+// also takes the 192 tile when its last round would otherwise be nearly
+// empty: when the CU work of its rounds, rounds x 192², is below that of the
+// 128 tile's, rounds x 2 x 128² (m = 8192: 4 rounds of 192 against 5 of 128,
+// the fifth holding 32 of 2080 tiles).  At shorter K the 192 tile, one MFMA
+// wave per SIMD, runs well below the 128 tile's rate.  min_m: the smallest
+// m of the launch's stacks.
+NS_HD constexpr int tri_class_of_tiles(int dtype, long long t128, long long t192, long long t256, bool gram,
+                                       long long min_m) {
+  return (dtype == 1 && (t128 < 1024 || (min_m >= 4096 && launch_rounds(t192, 256) * 192 * 192 <
+                                                               launch_rounds(t128, 512) * 2 * 128 * 128)))
+             ? TRI_WIDE
+         : (gram && dtype == 1 && t256 >= 1024) ? TRI_BIG
+                                                : TRI_NARROW;
 }
 NS_HD constexpr int tri_class(int dtype, long long batch, long long m, bool gram) {
-  return tri_class_of_tiles(dtype, tri_tiles(batch, m, 128), tri_tiles(batch, m, 256), gram);
+  return tri_class_of_tiles(dtype, tri_tiles(batch, m, 128), tri_tiles(batch, m, 192), tri_tiles(batch, m, 256), gram,
+                            m);
 }
 NS_HD constexpr TileCfg tile_cfg(int dtype, bool tri, int tri_cls = TRI_NARROW) {
   return dtype == 1 ? (tri ? (tri_cls == TRI_WIDE ? kTileBf16TriWide

@@ -151,17 +151,21 @@ struct TileChoice {
 };
 
 inline TileChoice choose_tiles(const Plan* ps, int n) {
-  long long t128[2] = {0, 0}, t256[2] = {0, 0};
+  long long t128[2] = {0, 0}, t192[2] = {0, 0}, t256[2] = {0, 0};
+  long long min_m[2] = {1LL << 40, 1LL << 40};
   int dtype = n > 0 ? ps[0].dtype : 1;
   for (int i = 0; i < n; ++i) {
     const Plan& p = ps[i];
     t128[p.tall] += tri_tiles(p.batch, p.m, 128);
+    t192[p.tall] += tri_tiles(p.batch, p.m, 192);
     t256[p.tall] += tri_tiles(p.batch, p.m, 256);
+    if (p.m < min_m[p.tall]) min_m[p.tall] = p.m;
   }
   TileChoice c;
-  c.gram_wide = tri_class_of_tiles(dtype, t128[0], t256[0], true);
-  c.gram_tall = tri_class_of_tiles(dtype, t128[1], t256[1], true);
-  c.poly = tri_class_of_tiles(dtype, t128[0] + t128[1], t256[0] + t256[1], false);
+  c.gram_wide = tri_class_of_tiles(dtype, t128[0], t192[0], t256[0], true, min_m[0]);
+  c.gram_tall = tri_class_of_tiles(dtype, t128[1], t192[1], t256[1], true, min_m[1]);
+  c.poly = tri_class_of_tiles(dtype, t128[0] + t128[1], t192[0] + t192[1], t256[0] + t256[1], false,
+                              min_m[0] < min_m[1] ? min_m[0] : min_m[1]);
   const TileCfg tp = tile_cfg(dtype, true, c.poly);
   bool ok = dtype == 1 && c.poly == TRI_NARROW;
   for (int o = 0; o < 2; ++o)
