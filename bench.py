@@ -39,7 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import newton_schulz_07_amd as ns  # noqa: E402
-from ns_inputs import WORKLOADS, make_workload  # noqa: E402
+from ns_inputs import WORKLOADS, gaussian, make_workload  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
@@ -324,9 +324,11 @@ def all_configs(prefix, steps, warmup):
         del xg, out, yd
         torch.cuda.empty_cache()
     grows = grouped_rows(steps, warmup)
+    orows = odd_shape_rows(steps, warmup)
     host = {"cpu_model": cpu_model(), "cores": len(os.sched_getaffinity(0))}
     with open(prefix + ".json", "w") as f:
-        json.dump({"measured_peak": peak, "host": host, "rows": rows, "grouped": grows}, f, indent=1)
+        json.dump({"measured_peak": peak, "host": host, "rows": rows, "grouped": grows, "odd_shapes": orows}, f,
+                  indent=1)
     lines = ["| workload | dtype | ms/call (p10-p90) | eff. TFLOP/s | % spec peak | % measured peak | dense ms | "
              "speedup vs dense | err max / mean | dense err | model floor | oracle s/slice | H200 dense / QuACK ms |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
@@ -345,6 +347,12 @@ def all_configs(prefix, steps, warmup):
     for r in grows:
         lines.append(f"| {r['set']} | {r['stacks']} | {r['singles_ms']:.3f} | {r['grouped_ms']:.3f} | "
                      f"{r['speedup']:.2f}x | {'yes' if r['bitwise_equal'] else 'NO'} |")
+    lines += ["", "Sides not multiples of 8 (the call runs on a zero-padded copy: the pad pass fused with the sum "
+              "of squares, and a vectorised copy of the caller's block out) beside the padded shape, bf16, "
+              "median ms per call:", "",
+              "| shape | ms | padded neighbour | ms | overhead |", "|---|---|---|---|---|"]
+    for r in orows:
+        lines.append(f"| {r['odd']} | {r['odd_ms']:.3f} | {r['even']} | {r['even_ms']:.3f} | {r['overhead_pct']:+.1f}% |")
     with open(prefix + ".md", "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines), flush=True)
@@ -380,6 +388,33 @@ def grouped_rows(steps, warmup):
         rows.append(row)
         print(json.dumps(row), flush=True)
         del xs, ya, yb
+        torch.cuda.empty_cache()
+    return rows
+
+
+ODD_PAIRS = [((16, 1535, 2047), (16, 1536, 2048)), ((1, 4095, 4095), (1, 4096, 4096)),
+             ((64, 2047, 767), (64, 2048, 768))]
+
+
+def odd_shape_rows(steps, warmup):
+    """Shapes whose sides are not multiples of 8 (run on zero-padded copies)
+    beside their padded neighbour: the median call time of each and the
+    overhead of the padded path."""
+    rows = []
+    for k, (odd, even) in enumerate(ODD_PAIRS):
+        res = {}
+        for label, shape in (("odd", odd), ("even", even)):
+            x = gaussian(shape, 2000 + 2 * k + (label == "even"), torch.bfloat16).to("cuda:0")
+            y = torch.empty_like(x)
+            for _ in range(warmup):
+                ns.orthogonalize(x, out=y)
+            torch.cuda.synchronize()
+            res[label + "_ms"] = float(np.median(call_times(lambda: ns.orthogonalize(x, out=y), max(5, steps // 2))))
+            del x, y
+        row = {"odd": "x".join(map(str, odd)), "even": "x".join(map(str, even)), **res,
+               "overhead_pct": 100.0 * (res["odd_ms"] / res["even_ms"] - 1.0)}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
         torch.cuda.empty_cache()
     return rows
 

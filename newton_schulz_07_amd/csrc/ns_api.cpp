@@ -194,12 +194,16 @@ hipError_t timed_launch(int kind, hipStream_t st, F&& f) {
 
 // ---------------------------------------------------------------- stages
 
-int run_normalize(const void* x, void* y, float* norms, const Plan& p, float* partials, hipStream_t st) {
+// sums_done: the partials are already there (a padded call's pad pass
+// computes them).
+int run_normalize(const void* x, void* y, float* norms, const Plan& p, float* partials, hipStream_t st,
+                  bool sums_done = false) {
   const NormArgs g = ns::norm_args(p, x, y, norms, partials);
   const int batch = (int)p.batch;
-  if (int s = check_hip(timed_launch(NS_KIND_SUMSQ, st, [&] { return ns::launch_sumsq(p.dtype, g, batch, st); }),
-                        "sum-of-squares launch"))
-    return s;
+  if (!sums_done)
+    if (int s = check_hip(timed_launch(NS_KIND_SUMSQ, st, [&] { return ns::launch_sumsq(p.dtype, g, batch, st); }),
+                          "sum-of-squares launch"))
+      return s;
   if (y == nullptr) return NS_OK;  // sums of squares only (folded normalisation)
   return check_hip(timed_launch(NS_KIND_SCALE, st, [&] { return ns::launch_scale(p.dtype, g, batch, st); }),
                    "scale launch");
@@ -371,29 +375,39 @@ int run_stacks(std::vector<Group>& gs, size_t ws_bytes, int ns_steps, float a, f
   launches[0] = launches[1] = launches[2] = 0;
 
   for (Group& g : gs) {
-    if (g.p.padded) {
-      const ns::PadArgs pa = ns::pad_args(g.p, g.uin, ws + g.ws_off + g.p.off_pin, true);
-      if (int s = check_hip(ns::launch_pad(dtype, pa, st), "pad launch")) return s;
+    if (g.p.padded) {  // the padded copy and its sums of squares in one pass
       g.in = ws + g.ws_off + g.p.off_pin;
       g.out = ws + g.ws_off + g.p.off_pout;
+      const ns::PadArgs pa = ns::pad_args(g.p, g.uin, const_cast<void*>(g.in), true);
+      const NormArgs na = ns::norm_args(g.p, g.in, nullptr, nullptr, g.part);
+      if (int s = check_hip(timed_launch(NS_KIND_SUMSQ, st,
+                                         [&] { return ns::launch_pad_sumsq(dtype, pa, na, (int)g.p.batch, st); }),
+                            "pad launch"))
+        return s;
     }
     g.copy_in = ns::input_copy_needed(ns_steps, g.in == g.out);
   }
   if (ns_steps == 0) {  // X0 = x / (||x||_F + eps), in place if out == in
     for (const Group& g : gs)
-      if (int s = run_normalize(g.in, g.out, nullptr, g.p, g.part, st)) return s;
+      if (int s = run_normalize(g.in, g.out, nullptr, g.p, g.part, st, g.p.padded)) return s;
   } else {
-    // one sum-of-squares launch over every stack; 1/||x|| rides in step 1
+    // one sum-of-squares launch over every stack not padded (the pad pass
+    // did those); 1/||x|| rides in step 1
     std::vector<NormArgs> na;
     std::vector<int> nb;
     for (const Group& g : gs) {
+      if (g.p.padded) continue;
       na.push_back(ns::norm_args(g.p, g.in, nullptr, nullptr, g.part));
       nb.push_back((int)g.p.batch);
     }
-    if (int s = check_hip(timed_launch(NS_KIND_SUMSQ, st,
-                                       [&] { return ns::launch_sumsq_grouped(dtype, na.data(), nb.data(), n, st); }),
-                          "sum-of-squares launch"))
-      return s;
+    if (!na.empty())
+      if (int s = check_hip(timed_launch(NS_KIND_SUMSQ, st,
+                                         [&] {
+                                           return ns::launch_sumsq_grouped(dtype, na.data(), nb.data(),
+                                                                           (int)na.size(), st);
+                                         }),
+                            "sum-of-squares launch"))
+        return s;
     for (const Group& g : gs)
       if (g.copy_in) {
         const size_t pb = (size_t)g.p.batch * g.p.rows * g.p.cols * esize(dtype);
@@ -444,7 +458,7 @@ int run_stacks(std::vector<Group>& gs, size_t ws_bytes, int ns_steps, float a, f
   for (const Group& g : gs)
     if (g.p.padded) {
       const ns::PadArgs pa = ns::pad_args(g.p, g.out, g.uout, false);
-      if (int s = check_hip(ns::launch_pad(dtype, pa, st), "unpad launch")) return s;
+      if (int s = check_hip(ns::launch_unpad(dtype, pa, st), "unpad launch")) return s;
     }
   return NS_OK;
 }

@@ -555,20 +555,33 @@ void replay_norm_grouped(const std::vector<NormArgs>& gs, const std::vector<int>
   }
 }
 
-// Pad or unpad (mirrors pad_kernel): destination element e of every slice,
-// first and last of each destination row, reads and writes in bounds.
+// Pad (mirrors pad_sumsq_kernel's gathers; its vector ranges and partials
+// are those of the sum-of-squares replay over the padded copy) or unpad
+// (mirrors unpad_kernel): the first and last 16-byte vector of every row
+// visited, through the kernels' own pad_vec, with every element read or
+// written in bounds.
 void replay_pad(const PadArgs& g, int es, const char* what) {
-  const long long dr = g.to_padded ? g.rows : g.urows, dc = g.to_padded ? g.cols : g.ucols;
   if (g.urows > g.rows || g.ucols > g.cols || g.rows % 8 || g.cols % 8) fail(std::string(what) + ": bad padded shape");
+  if (g.rows * g.cols >= (1LL << 29)) fail(std::string(what) + ": slice too large for 32-bit vector indexes");
+  const int epv = 16 / es, vpr = (int)(g.cols / epv);
+  const long long rows_v = g.to_padded ? g.rows : g.urows;
   for (long long b = 0; b < g.batch; ++b)
-    for (long long i = 0; i < dr; ++i)
-      for (long long j : {0LL, dc - 1}) {
-        const long long e = (b * dr + i) * dc + j;
-        access(g.dst, e * es, es, what);
+    for (long long i = 0; i < rows_v; ++i)
+      for (int c : {0, vpr - 1}) {
+        const int v = (int)(i * vpr + c);
+        int r, j0;
+        pad_vec(v, vpr, epv, &r, &j0);
+        if (r != i || j0 != c * epv) fail(std::string(what) + ": pad_vec maps a vector to the wrong place");
+        const long long padded_vec = (b * g.rows * vpr + v) * 16;
         if (g.to_padded) {
-          if (i < g.urows && j < g.ucols) access(g.src, ((b * g.urows + i) * g.ucols + j) * es, es, what);
+          access(g.dst, padded_vec, 16, what);
+          for (int k = 0; k < epv; ++k)
+            if (r < g.urows && j0 + k < g.ucols) access(g.src, ((b * g.urows + r) * g.ucols + j0 + k) * es, es, what);
         } else {
-          access(g.src, ((b * g.rows + i) * g.cols + j) * es, es, what);
+          if (j0 >= g.ucols) continue;  // a vector wholly in the padding is not read
+          access(g.src, padded_vec, 16, what);
+          for (int k = 0; k < epv; ++k)
+            if (j0 + k < g.ucols) access(g.dst, ((b * g.urows + r) * g.ucols + j0 + k) * es, es, what);
         }
       }
 }
@@ -684,13 +697,19 @@ void replay_grouped_call(int dtype, int steps, const std::vector<Shape>& shapes,
   for (const G& g : gs) plans.push_back(g.p);
   const TileChoice tc = choose_tiles(plans.data(), (int)plans.size());
   {
+    // padded stacks: the pad pass computes their sums of squares (the same
+    // blocks over the padded copy); the grouped launch covers the others
     std::vector<NormArgs> na;
     std::vector<int> nb;
     for (const G& g : gs) {
+      if (g.p.padded) {
+        replay_norm(norm_args(g.p, g.in, nullptr, nullptr, g.part), (int)g.p.batch, false, "pad sumsq");
+        continue;
+      }
       na.push_back(norm_args(g.p, g.in, nullptr, nullptr, g.part));
       nb.push_back((int)g.p.batch);
     }
-    replay_norm_grouped(na, nb, "grouped sumsq");
+    if (!na.empty()) replay_norm_grouped(na, nb, "grouped sumsq");
   }
   auto wbuf = [&](const G& g, int s) -> void* { return iterate_in_out(steps, s) ? g.out : g.xtmp; };
   auto buf = [&](const G& g, int s) -> void* { return s == 0 ? (g.copy_in ? g.xtmp : g.in) : wbuf(g, s); };

@@ -20,7 +20,10 @@ hipError_t launch_gemm_grouped(int dtype, const StageKind& k, const GemmArgs* gs
 hipError_t launch_sumsq(int dtype, const NormArgs& g, int batch, hipStream_t st);
 hipError_t launch_sumsq_grouped(int dtype, const NormArgs* gs, const int* batch, int n, hipStream_t st);
 hipError_t launch_scale(int dtype, const NormArgs& g, int batch, hipStream_t st);
-hipError_t launch_pad(int dtype, const PadArgs& g, hipStream_t st);
+// odd shapes: the zero-padded copy fused with the sum-of-squares pass (g
+// over the padded copy), and the caller's block out of the padded result
+hipError_t launch_pad_sumsq(int dtype, const PadArgs& p, const NormArgs& g, int batch, hipStream_t st);
+hipError_t launch_unpad(int dtype, const PadArgs& p, hipStream_t st);
 
 // Device address of the fixed scratch array (ns_noalloc.hip) on device
 // `dev`, which must be the current device.  The first call per device takes

@@ -825,23 +825,67 @@ __global__ __launch_bounds__(kNormThreads) void scale_kernel(const NormArgs g) {
 
 // --------------------------------------------------- padding (odd shapes)
 
-// One element of the destination per thread (grid-stride): pad writes the
-// whole padded slice (zeros outside the caller's rows x cols), unpad reads
-// the caller's block back out of the padded result.
+// The zero-padded copy of a slice and its partial sums of squares in one
+// pass.  Block (chunk, slice) covers the same vectors of the padded slice,
+// thread by thread, as sumsq_kernel does over the padded copy, so the
+// partials are bitwise the ones that kernel would compute from it; each
+// vector is gathered element by element from the caller's rows (not 16-byte
+// aligned), zero outside them.
 template <typename T>
-__global__ __launch_bounds__(256) void pad_kernel(const PadArgs g) {
-  const T* src = reinterpret_cast<const T*>(g.src);
-  T* dst = reinterpret_cast<T*>(g.dst);
-  const long long dr = g.to_padded ? g.rows : g.urows, dc = g.to_padded ? g.cols : g.ucols;
-  const long long total = g.batch * dr * dc;
-  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (long long)gridDim.x * blockDim.x) {
-    const long long b = e / (dr * dc), r = e % (dr * dc);
-    const long long i = r / dc, j = r % dc;
-    if (g.to_padded)
-      dst[e] = (i < g.urows && j < g.ucols) ? src[(b * g.urows + i) * g.ucols + j] : T(0.0f);
-    else
-      dst[e] = src[(b * g.rows + i) * g.cols + j];
+__global__ __launch_bounds__(kNormThreads) void pad_sumsq_kernel(const PadArgs p, const NormArgs g) {
+  __shared__ float red[kNormThreads / 64];
+  constexpr int EPV = Elem<T>::kChunk;
+  const int slice = blockIdx.y, chunk = blockIdx.x;
+  const T* src = reinterpret_cast<const T*>(p.src) + (size_t)slice * p.urows * p.ucols;
+  uint4* dst = reinterpret_cast<uint4*>(p.dst) + (size_t)slice * g.slice_vecs;
+  const int vpr = (int)(p.cols / EPV), urows = (int)p.urows, ucols = (int)p.ucols;
+  const int v0 = (int)((long long)chunk * g.chunk_vecs);
+  const int v1 = (int)((v0 + g.chunk_vecs < g.slice_vecs) ? v0 + g.chunk_vecs : g.slice_vecs);
+  float s = 0.0f;
+  for (int v = v0 + (int)threadIdx.x; v < v1; v += kNormThreads) {
+    int i, j0;
+    pad_vec(v, vpr, EPV, &i, &j0);
+    T e[EPV];
+#pragma unroll
+    for (int k = 0; k < EPV; ++k)
+      e[k] = (i < urows && j0 + k < ucols) ? src[(size_t)i * ucols + j0 + k] : T(0.0f);
+    uint4 val;
+    __builtin_memcpy(&val, e, 16);
+    dst[v] = val;
+    s += sumsq16(val, T());
+  }
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kNormThreads / 64; ++w) t += red[w];
+    g.partials[(size_t)slice * g.chunks + chunk] = t;
+  }
+}
+
+// The caller's block out of a padded result: one 16-byte vector of the
+// padded slice's first urows rows per thread (grid-stride in x, slice in y),
+// its elements inside the caller's columns stored one by one.
+template <typename T>
+__global__ __launch_bounds__(256) void unpad_kernel(const PadArgs p) {
+  constexpr int EPV = Elem<T>::kChunk;
+  const int slice = blockIdx.y;
+  const int vpr = (int)(p.cols / EPV), ucols = (int)p.ucols;
+  const int nv = (int)p.urows * vpr;
+  const uint4* src = reinterpret_cast<const uint4*>(p.src) + (size_t)slice * p.rows * vpr;
+  T* dst = reinterpret_cast<T*>(p.dst) + (size_t)slice * p.urows * p.ucols;
+  for (int v = blockIdx.x * 256 + (int)threadIdx.x; v < nv; v += gridDim.x * 256) {
+    int i, j0;
+    pad_vec(v, vpr, EPV, &i, &j0);
+    if (j0 >= ucols) continue;
+    const uint4 val = src[v];
+    T e[EPV];
+    __builtin_memcpy(e, &val, 16);
+#pragma unroll
+    for (int k = 0; k < EPV; ++k)
+      if (j0 + k < ucols) dst[(size_t)i * ucols + j0 + k] = e[k];
   }
 }
 
@@ -957,12 +1001,19 @@ hipError_t launch_gemm_grouped(int dtype, const StageKind& k, const GemmArgs* gs
   return dispatch_mode<float>(k, gs, n, st);
 }
 
-hipError_t launch_pad(int dtype, const PadArgs& g, hipStream_t st) {
-  const long long total = g.batch * (g.to_padded ? g.rows * g.cols : g.urows * g.ucols);
-  const long long want = (total + 255) / 256;
-  const unsigned blocks = (unsigned)(want < 65536 ? (want > 0 ? want : 1) : 65536);
-  if (dtype == 1) dispatch(pad_kernel<bf16>, dim3(blocks), dim3(256), st, g);
-  else dispatch(pad_kernel<float>, dim3(blocks), dim3(256), st, g);
+hipError_t launch_pad_sumsq(int dtype, const PadArgs& p, const NormArgs& g, int batch, hipStream_t st) {
+  dim3 grid(g.chunks, batch);
+  if (dtype == 1) dispatch(pad_sumsq_kernel<bf16>, grid, dim3(kNormThreads), st, p, g);
+  else dispatch(pad_sumsq_kernel<float>, grid, dim3(kNormThreads), st, p, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpad(int dtype, const PadArgs& p, hipStream_t st) {
+  const long long vecs = p.urows * (p.cols / elems_per_chunk(dtype));
+  const long long want = (vecs + 255) / 256;
+  const unsigned bx = (unsigned)(want < 4096 ? (want > 0 ? want : 1) : 4096);
+  if (dtype == 1) dispatch(unpad_kernel<bf16>, dim3(bx, (unsigned)p.batch), dim3(256), st, p);
+  else dispatch(unpad_kernel<float>, dim3(bx, (unsigned)p.batch), dim3(256), st, p);
   return hipGetLastError();
 }
 

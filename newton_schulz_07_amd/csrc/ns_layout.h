@@ -377,6 +377,15 @@ NS_HD int launch_group(int lin, const int* start, int n) {
   return grp;
 }
 
+// Zero-padded copies of odd shapes, by 16-byte vectors: vector v of a padded
+// slice (vpr vectors per row) holds row v / vpr, columns (v % vpr) epv ..
+// + epv - 1 (epv elements per vector).  32-bit: a slice has fewer than 2^29
+// elements.
+NS_HD void pad_vec(int v, int vpr, int epv, int* row, int* col0) {
+  *row = v / vpr;
+  *col0 = (v - *row * vpr) * epv;
+}
+
 // Normalisation: per-slice sum of squares over 32 KiB blocks, then a scale
 // pass over the same blocks.
 struct NormArgs {

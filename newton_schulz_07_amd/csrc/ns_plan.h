@@ -77,8 +77,9 @@ inline Plan make_plan(int64_t batch, int64_t urows, int64_t ucols, int dtype) {
   return p;
 }
 
-// Zero-padded copy in (pad) or the caller's block out (unpad) of a padded
-// plan: one thread per element of the destination.
+// Zero-padded copy in (pad, fused with the sum-of-squares pass) or the
+// caller's block out (unpad) of a padded plan, by 16-byte vectors of the
+// padded slice (pad_vec).
 struct PadArgs {
   const void* src;
   void* dst;
