@@ -232,6 +232,11 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
     int ti, tj;
     if (tri) tri_decode(q, ti, tj);
     else rect_decode(q, g.tiles_m, g.tiles_n, ti, tj);
+    // the kernel's wave column (diagonal triangle tiles remap row half 1)
+    auto wave_col = [&](int wm_, int wn_) {
+      const bool remap = tri && t.wm == 2 && t.wn == 4 && t.lw == 0 && !(t.bm == 256 && kind.p_nat);
+      return remap ? tri_wave_col(wm_, wn_, t.wn, ti == tj) : wn_;
+    };
     if (slice >= g.batch || ti < 0 || tj < 0 || ti >= g.tiles_m || tj >= g.tiles_n || (tri && tj > ti)) {
       fail(std::string(what) + ": tile decode out of range");
       continue;
@@ -290,7 +295,7 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
         continue;  // the kernel compiles no capture in its natural-layout phase
       }
       for (int tid = 0; tid < NT; ++tid) {
-        const int lane = tid & 63, wave = tid >> 6, wm = wave / t.wn, wn = wave % t.wn;
+        const int lane = tid & 63, wave = tid >> 6, wm = wave / t.wn, wn = wave_col(wm, wave % t.wn);
         if (mode == MODE_UPD_ROW) {
           for (int a = 0; a < SM; ++a) {
             const int ib = i0 + wm * WTM + a * 32;
@@ -336,7 +341,7 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
     const long long ob = (long long)slice * g.o_bs, db = (long long)slice * g.d_bs;
     const int qsz = 4 * es;  // bytes of 4 consecutive elements
     for (int tid = 0; tid < NT; ++tid) {
-      const int lane = tid & 63, wave = tid >> 6, wm = wave / t.wn, wn = wave % t.wn;
+      const int lane = tid & 63, wave = tid >> 6, wm = wave / t.wn, wn = wave_col(wm, wave % t.wn);
       for (int a = 0; a < SM; ++a) {
         const int il = wm * WTM + a * 32 + acc_i(lane), i = i0 + il;
         for (int b = 0; b < SN; ++b)
@@ -789,8 +794,41 @@ void check_group_map() {
   }
 }
 
+// The diagonal tiles' wave columns are a permutation within each row half,
+// and the blocks they skip lie wholly above the diagonal.
+void check_diag_waves() {
+  for (int wm = 0; wm < 2; ++wm) {
+    int seen = 0;
+    for (int wn = 0; wn < 4; ++wn) seen |= 1 << tri_wave_col(wm, wn, 4, true);
+    if (seen != 0xF) fail("tri_wave_col is not a permutation of the wave columns");
+  }
+  for (int bm : {128, 256}) {
+    const int SM = bm / 2 / 32, SN = bm / 4 / 32, nb = bm / 32;
+    std::vector<int> per_simd(4, 0), needed(nb * nb, 0);
+    for (int wave = 0; wave < 8; ++wave) {
+      const int wm = wave / 4, wn = tri_wave_col(wm, wave % 4, 4, true);
+      for (int a = 0; a < SM; ++a)
+        for (int b = 0; b < SN; ++b) {
+          const int rb = wm * SM + a, cb = wn * SN + b;
+          const bool above = tri_block_above(wm, wn, a, b, SM, SN);
+          if (above != (cb > rb)) fail("tri_block_above disagrees with the block's position");
+          if (!above) {
+            per_simd[wave % 4]++;
+            needed[rb * nb + cb]++;
+          }
+        }
+    }
+    for (int rb = 0; rb < nb; ++rb)
+      for (int cb = 0; cb < nb; ++cb)
+        if (needed[rb * nb + cb] != (cb <= rb ? 1 : 0)) fail("a block on or below the diagonal is not computed once");
+    const int mx = *std::max_element(per_simd.begin(), per_simd.end());
+    if (mx > (bm == 256 ? 10 : 3)) fail("diagonal-tile blocks are not balanced over the SIMDs");
+  }
+}
+
 int main(int argc, char** argv) {
   check_group_map();
+  check_diag_waves();
   // grouped call: --group dtype steps b r c [b r c ...]
   if (argc >= 7 && std::string(argv[1]) == "--group" && (argc - 4) % 3 == 0) {
     const int dtype = std::atoi(argv[2]), steps = std::atoi(argv[3]);

@@ -215,7 +215,7 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool mw = LW == 0 || wave < WM * WN;  // an MFMA wave (wave-uniform)
-  const int wm = (mw ? wave : 0) / WN, wn = (mw ? wave : 0) % WN;
+  const int wm = (mw ? wave : 0) / WN;
 
   int grp = 0, lin;
   if constexpr (NG > 1) lin = xcd_group_tile(blockIdx.x, gridDim.x, L.start, L.n, &grp);
@@ -227,6 +227,20 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
   if (mode_is_tri(MODE)) tri_decode(q, ti, tj);
   else rect_decode(q, g.tiles_m, g.tiles_n, ti, tj);
   const int i0 = ti * BM, j0 = tj * BN;
+  // diagonal triangle tiles with 2 x 4 MFMA waves: SIMD-balanced wave
+  // columns, and no MFMAs for blocks wholly above the diagonal (tri_wave_col).
+  // Not the 256 tile on natural-layout operands (the tall Gram): it already
+  // spills, and the skip made it slower.
+  constexpr bool DIAG_SKIP = mode_is_tri(MODE) && WM == 2 && WN == 4 && LW == 0 && !(BM == 256 && PL == LAY_NAT);
+  const int wn = DIAG_SKIP ? tri_wave_col(wm, (mw ? wave : 0) % WN, WN, ti == tj) : (mw ? wave : 0) % WN;
+  uint32_t above = 0;  // bit a * SN + b: block (a, b) is not computed
+  if (DIAG_SKIP && ti == tj) {
+#pragma unroll
+    for (int a = 0; a < SM; ++a)
+#pragma unroll
+      for (int b = 0; b < SN; ++b)
+        if (tri_block_above(wm, wn, a, b, SM, SN)) above |= 1u << (a * SN + b);
+  }
   // first stage an operand reads in its natural layout (never: a large value)
   const int nat_from_p = PL == LAY_SYM ? sym_nat_from(i0, g.sym_tile, BK) : (PNAT ? 0 : 0x7fffffff);
   const int nat_from_q = QL == LAY_SYM ? sym_nat_from(j0, g.sym_tile, BK) : (QNAT ? 0 : 0x7fffffff);
@@ -420,7 +434,8 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
 #pragma unroll
       for (int a = 0; a < SM; ++a)
 #pragma unroll
-        for (int b = 0; b < SN; ++b) mfma_chunk(acc[a][b], qf[s & 1][b], pf[s & 1][a], T());
+        for (int b = 0; b < SN; ++b)
+          if (!DIAG_SKIP || !((above >> (a * SN + b)) & 1u)) mfma_chunk(acc[a][b], qf[s & 1][b], pf[s & 1][a], T());
       if (STAGGER && s == issue_step) {
         __builtin_amdgcn_sched_barrier(0);
         late();

@@ -282,6 +282,21 @@ NS_HD constexpr bool sym_layout_ok(int rows, int sym_tile, int bk, int st) {
   return sym_tile > 0 && sym_tile % bk == 0 && (sym_tile / bk) % st == 0 && rows <= sym_tile;
 }
 
+// Diagonal tiles of the triangle kernels with 2 x 4 MFMA waves: only their
+// 32 x 32 blocks on or below the diagonal are computed (the others are
+// replaced by the mirror of the lower half when stored), and the waves of
+// tile row half 1 take the columns in the order 3, 2, 0, 1, so that the two
+// waves of each SIMD (w and w + 4) hold about the same number of those
+// blocks: 10, 10, 8, 8 of 16 block products per k step on a 256 tile
+// instead of 15, 11, 7, 3; 3, 3, 2, 2 of 4 on a 128 tile instead of
+// 4, 3, 2, 1.
+NS_HD int tri_wave_col(int wm, int wn, int wn_count, bool diag) {
+  return (diag && wm == 1 && wn_count == 4) ? (0x1023 >> (4 * wn)) & 0xF : wn;
+}
+// Block (a, b) of the wave at (wm, wn) (sm x sn blocks per wave) lies wholly
+// above the diagonal of a diagonal tile.
+NS_HD bool tri_block_above(int wm, int wn, int a, int b, int sm, int sn) { return wn * sn + b > wm * sm + a; }
+
 // MFMA operand roles: the A operand is the Q tile (output column j), the B
 // operand the P tile (output row i).  Register r of lane l of a 32x32 block
 // then holds row i = l % 32 and column j = 8 (r / 4) + 4 (l / 32) + r % 4,
