@@ -26,7 +26,9 @@ import torch
 
 import newton_schulz_07_amd as ns
 from ns_inputs import WORKLOADS, make_workload
-from oracle import newton_schulz
+from oracle import newton_schulz, newton_schulz_batched
+from oracle.ns_oracle import DEFAULT_COEFFS, EPS, ns_iteration
+from ns_inputs import gaussian
 from tests.gpu_util import device, rel_err, report, to64
 
 pytestmark = pytest.mark.gpu
@@ -138,3 +140,53 @@ def test_bf16_at_least_as_accurate_as_dense_bf16(name):
             "max_dense": max(d for _, d in errs.values())})
     for i, (e, ed) in errs.items():
         assert e <= ed, (i, e, ed)
+
+
+@pytest.mark.parametrize("dtype,bar", [(torch.bfloat16, 1e-2), (torch.float32, 1e-4)])
+def test_max_slice_block_diagonal(dtype, bar):
+    # a 16384 x 16384 slice (2^28 elements, the largest power-of-two square
+    # under the 2^29-element slice limit), block diagonal with four 4096 x
+    # 4096 blocks.  A = X Xᵀ, C and every iterate stay block diagonal, so the
+    # off-diagonal blocks of the result are exactly zero, and diagonal block
+    # b is the oracle's iteration applied to X_b / (||X||_F + eps): the
+    # normalisation is the whole matrix's, so each block is checked with the
+    # oracle's step function at that global scale.
+    n, k = 16384, 4096
+    blocks = [gaussian((k, k), 1700 + b, torch.float32) * (0.5 + b) for b in range(4)]
+    x = torch.zeros(n, n, dtype=torch.float32)
+    for b, xb in enumerate(blocks):
+        x[b * k:(b + 1) * k, b * k:(b + 1) * k] = xb
+    x = x.to(dtype)
+    y = ns.orthogonalize(x.to(device()))
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all()
+    mask = torch.ones(n, n, dtype=torch.bool, device=y.device)
+    for b in range(4):
+        mask[b * k:(b + 1) * k, b * k:(b + 1) * k] = False
+    assert int(torch.count_nonzero(y[mask])) == 0, "off-diagonal blocks are not exactly zero"
+    xd = x.double().numpy()
+    nrm = float(np.sqrt(sum(float((x[b * k:(b + 1) * k, b * k:(b + 1) * k].double() ** 2).sum()) for b in range(4))))
+    a, bb, c = DEFAULT_COEFFS
+    errs = []
+    for b in range(4):
+        z = xd[b * k:(b + 1) * k, b * k:(b + 1) * k] / (nrm + EPS)
+        for _ in range(5):
+            z = ns_iteration(z, a, bb, c)
+        got = to64(y[b * k:(b + 1) * k, b * k:(b + 1) * k])
+        errs.append(float(np.linalg.norm(got - z) / np.linalg.norm(z)))
+    report({"case": f"max_slice_block_diagonal_{dtype}", "errs": errs})
+    assert max(errs) <= bar, errs
+
+
+def test_max_batch():
+    # 65535 slices (the batch limit) of 8 x 16, bf16: every slice finite,
+    # sampled slices against the oracle
+    x = gaussian((65535, 8, 16), 1750, torch.float32)
+    y = ns.orthogonalize(x.to(torch.bfloat16).to(device()))
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all()
+    idx = [0, 1, 4095, 32767, 65534]
+    ref = newton_schulz_batched(x.to(torch.bfloat16).double().numpy(), slices=idx)
+    e = rel_err(to64(y[idx]), ref)
+    report({"case": "max_batch", "errs": e.tolist()})
+    assert e.max() <= 1e-2, e
