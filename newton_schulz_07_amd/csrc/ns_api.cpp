@@ -251,10 +251,12 @@ void record_config(const Plan& p, int steps) {
                 tg.wn, tg.lw, tg.cpr * 16, tg.st, p.tall ? "columns(transposed-read)" : "rows", tp.bm, tp.bn, tp.wm, tp.wn,
                 tp.cpr * 16, tp.st, p.tall ? "X*C" : "C*X", tr.bm, tr.bn, tr.wm, tr.wn, tr.cpr * 16, tr.st,
                 p.tall ? "rows" : "columns(transposed-read)",
-                ns::late_issue_tiles(p.dtype, (long long)ns::tiles_of(p.rows, tr.bm) * ns::tiles_of(p.cols, tr.bn) *
-                                                  p.batch)
+                ns::late_issue(p.dtype, (long long)ns::tiles_of(p.rows, tr.bm) * ns::tiles_of(p.cols, tr.bn) * p.batch,
+                               (int)p.m)
                     ? "after-first-k-step"
-                    : "stage-start");
+                    : (p.dtype == NS_DTYPE_BF16 && ns::update_k_stages((int)p.m) >= ns::kStaggerMinStages
+                           ? "staggered"
+                           : "stage-start"));
   t_cfg = buf;
   if (p.padded)
     t_cfg += " | zero-padded from " + std::to_string(p.urows) + "x" + std::to_string(p.ucols) + " to " +

@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "ns_kernels.h"
@@ -968,13 +969,18 @@ static hipError_t launch_tri(int cls, const GemmArgs* gs, int n, hipStream_t st)
   }
 }
 
-// The late load issue of the update: bf16 launches of at most
-// kLateIssueMaxTiles tiles over all their groups.
+// The late load issue of the update (late_issue): bf16 launches of at most
+// kLateIssueMaxTiles tiles over all their groups, or with no group long
+// enough for the staggered issue.
 template <typename T>
 static bool late_issue_of(const GemmArgs* gs, int n) {
   long long tiles = 0;
-  for (int i = 0; i < n; ++i) tiles += (long long)gs[i].tiles_per_slice * gs[i].batch;
-  return late_issue_tiles(std::is_same<T, bf16>::value ? 1 : 0, tiles);
+  int max_k = 0;
+  for (int i = 0; i < n; ++i) {
+    tiles += (long long)gs[i].tiles_per_slice * gs[i].batch;
+    max_k = std::max(max_k, gs[i].K);
+  }
+  return late_issue(std::is_same<T, bf16>::value ? 1 : 0, tiles, max_k);
 }
 
 template <typename T>

@@ -257,13 +257,23 @@ inline GemmArgs poly_args(const Plan& p, const void* oa, const float* da, void* 
 // Update launches of at most this many tiles (four rounds on 256 CUs) issue
 // each stage's operand loads after the stage's first k step rather than
 // before it: their MFMA work, not their loads, sets their pace, and the
-// loads then leave the MFMAs' start alone.  Launches with more tiles wait on
-// their loads and keep the early issue.
+// loads then leave the MFMAs' start alone.
 constexpr long long kLateIssueMaxTiles = 1024;
 // Larger bf16 update launches with at least this many K stages stagger the
 // load issue of the two tile-row halves by one k step (see the kernel).
+// Larger launches too short for that (no group with this many stages) take
+// the late issue: on 128 slices of 2048 x 768 (K = 768, 12 stages) it beats
+// issuing at the barrier, while on the long-K stacks the stagger beats it.
 constexpr int kStaggerMinStages = 16;
-inline bool late_issue_tiles(int dtype, long long tiles) { return dtype == 1 && tiles <= kLateIssueMaxTiles; }
+// K stages of a bf16 update launch over K (its k step: cpr chunks of 8).
+inline int update_k_stages(int K) {
+  const int bk = kTileBf16Rect.cpr * 8;
+  return (K + bk - 1) / bk;
+}
+// tiles: over all groups of the launch; max_k: the largest K among them
+inline bool late_issue(int dtype, long long tiles, int max_k) {
+  return dtype == 1 && (tiles <= kLateIssueMaxTiles || update_k_stages(max_k) < kStaggerMinStages);
+}
 
 // X' = C X (rows <= cols) or X C (rows > cols), C = O_C + diag(d_C).
 inline GemmArgs update_args(const Plan& p, const void* x, const void* oc, const float* dc, void* xo,
