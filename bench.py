@@ -329,7 +329,15 @@ def all_configs(prefix, steps, warmup):
     with open(prefix + ".json", "w") as f:
         json.dump({"measured_peak": peak, "host": host, "rows": rows, "grouped": grows, "odd_shapes": orows}, f,
                   indent=1)
-    lines = ["| workload | dtype | ms/call (p10-p90) | eff. TFLOP/s | % spec peak | % measured peak | dense ms | "
+    lines = ["# ns_orthogonalize on every workload: time, accuracy, the dense comparator, grouped calls, odd sides",
+             "", "Command (MI355X, one GPU; `$REPO` is the repository root):", "", "```",
+             f"python $REPO/bench.py --all-configs $REPO/gpurun_out/prof/all_configs --warmup {warmup} --steps {steps}",
+             "```", "",
+             f"This box: register-only MFMA loop {peak['tflops']:.0f} TFLOP/s at a {peak['shader_clock_mhz']:.0f} MHz "
+             f"shader clock; {host['cores']} host cores ({host['cpu_model']}).  Kernel source hash "
+             f"`{kernel_source_hash()}`.  Per workload: {warmup} warmup calls, then {steps} calls timed one by one; "
+             "errors are relative Frobenius errors against the fp64 oracle on the sampled slices.", "",
+             "| workload | dtype | ms/call (p10-p90) | eff. TFLOP/s | % spec peak | % measured peak | dense ms | "
              "speedup vs dense | err max / mean | dense err | model floor | oracle s/slice | H200 dense / QuACK ms |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
