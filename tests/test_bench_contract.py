@@ -30,7 +30,7 @@ def test_more_than_one_gpu_is_refused():
 
 @pytest.mark.gpu
 def test_short_run_prints_one_complete_line():
-    r = run_bench("--steps", "5", "--warmup", "2", "--also", "--cpu-budget", "0", "--no-dense")
+    r = run_bench("--steps", "5", "--warmup", "2", "--also", "--cpu-budget", "0", "--no-dense", "--sustain", "1")
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
     assert len(lines) == 1, r.stdout[-2000:]
@@ -53,3 +53,7 @@ def test_short_run_prints_one_complete_line():
     assert d["norm_pass"] is not None and 0.0 < d["norm_pass"]["frac"] < 1.0
     assert d["cpu_baseline"] is None  # --cpu-budget 0
     assert d["vs_baseline"] is None  # the pages' H200 figure is context only
+    sus = d["sustained"]  # back-to-back calls after the timed region, outside it
+    assert [s["name"] for s in sus] == ["lowrank64_4096x4096"]
+    assert sus[0]["seconds"] >= 1.0 and sus[0]["calls"] > 0 and sus[0]["ms_per_call"] > 0
+    assert sus[0]["eff_tflops"] == pytest.approx(dense_eq / (sus[0]["ms_per_call"] * 1e-3) / 1e12, rel=1e-6)
