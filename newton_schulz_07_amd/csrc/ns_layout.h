@@ -41,7 +41,7 @@ struct TileCfg {
 #define NS_TILE_BF16_TRI {128, 128, 2, 4, 8, 2, 2}
 #endif
 #ifndef NS_TILE_BF16_TRI_WIDE
-#define NS_TILE_BF16_TRI_WIDE {192, 192, 2, 2, 8, 2, 1, 4}
+#define NS_TILE_BF16_TRI_WIDE {192, 192, 6, 2, 8, 2, 1}
 #endif
 #ifndef NS_TILE_BF16_TRI_BIG
 #define NS_TILE_BF16_TRI_BIG {256, 256, 2, 4, 8, 2, 1}
@@ -67,12 +67,10 @@ constexpr TileCfg kTileF32Rect = NS_TILE_F32_RECT;
 // triangle tiles (fewer than two rounds of 512 workgroup slots at 128) would
 // leave a nearly empty last round, so it takes the larger tile instead
 // (m = 4096: 528 tiles at 128, 253 tiles at 192 on 256 CUs).
-// The 192 tile runs 4 MFMA waves (one per SIMD, 96 x 96 each) beside 4
-// loader waves: a workgroup's rate of LDS-direct loads grows with the number
-// of waves issuing them (from L2, about 22 B/clk per CU with 4 waves and 35
-// with 8), and the 192 tile needs a byte per 96 flops, which 4 waves alone
-// cannot feed.  Its poly then reads O_A in the epilogue instead of holding
-// the captured quads in registers.
+// The 192 tile runs 12 MFMA waves of 32 x 96 (6 x 2), three per SIMD, so
+// that while one wave waits for its fragment reads the other two keep the
+// matrix core busy, and 12 waves share each stage's LDS-direct loads (four
+// instructions each).  Its 36 blocks of 32 x 32 do not split over 8 waves.
 // Lower-triangle tiles of `tile` rows over a stack of m x m results.
 NS_HD constexpr long long tri_tiles(long long batch, long long m, int tile) {
   return batch * ((m + tile - 1) / tile) * ((m + tile - 1) / tile + 1) / 2;
@@ -91,9 +89,8 @@ NS_HD constexpr long long launch_rounds(long long tiles, long long slots) { retu
 // also takes the 192 tile when its last round would otherwise be nearly
 // empty: when the CU work of its rounds, rounds x 192², is below that of the
 // 128 tile's, rounds x 2 x 128² (m = 8192: 4 rounds of 192 against 5 of 128,
-// the fifth holding 32 of 2080 tiles).  At shorter K the 192 tile, one MFMA
-// wave per SIMD, runs well below the 128 tile's rate.  min_m: the smallest
-// m of the launch's stacks.
+// the fifth holding 32 of 2080 tiles).  At shorter K the 192 tile runs below
+// the 128 tile's rate.  min_m: the smallest m of the launch's stacks.
 NS_HD constexpr int tri_class_of_tiles(int dtype, long long t128, long long t192, long long t256, bool gram,
                                        long long min_m) {
   return (dtype == 1 && (t128 < 1024 || (min_m >= 4096 && launch_rounds(t192, 256) * 192 * 192 <
