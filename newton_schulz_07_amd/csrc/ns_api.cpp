@@ -242,13 +242,13 @@ void record_config(const Plan& p, int steps) {
   char buf[768];
   std::snprintf(buf, sizeof(buf),
                 "dtype=%s batch=%lld rows=%lld cols=%lld m=%lld %s steps=%d | norm: %s (%lldx16B blocks) | "
-                "mfma=%s | gram: lower-tri tile=%dx%d waves=%dx%d+%d k=%dB ring=%d operands=%s | poly: lower-tri "
+                "mfma=%s | gram: lower-tri tile=%dx%d waves=%dx%d k=%dB ring=%d operands=%s | poly: lower-tri "
                 "tile=%dx%d waves=%dx%d k=%dB ring=%d | update: %s tile=%dx%d waves=%dx%d k=%dB ring=%d X-operand=%s loads=%s",
                 p.dtype == NS_DTYPE_BF16 ? "bf16" : "fp32", (long long)p.batch, (long long)p.rows,
                 (long long)p.cols, (long long)p.m, p.tall ? "tall" : "wide", steps,
                 ns::fold_normalisation(steps) ? "sumsq, 1/||x|| folded into step 1" : "sumsq+scale",
                 ns::kNormChunkVecs, p.dtype == NS_DTYPE_BF16 ? "32x32x16_bf16" : "32x32x2_f32", tg.bm, tg.bn, tg.wm,
-                tg.wn, tg.lw, tg.cpr * 16, tg.st, p.tall ? "columns(transposed-read)" : "rows", tp.bm, tp.bn, tp.wm, tp.wn,
+                tg.wn, tg.cpr * 16, tg.st, p.tall ? "columns(transposed-read)" : "rows", tp.bm, tp.bn, tp.wm, tp.wn,
                 tp.cpr * 16, tp.st, p.tall ? "X*C" : "C*X", tr.bm, tr.bn, tr.wm, tr.wn, tr.cpr * 16, tr.st,
                 p.tall ? "rows" : "columns(transposed-read)",
                 ns::late_issue(p.dtype, (long long)ns::tiles_of(p.rows, tr.bm) * ns::tiles_of(p.cols, tr.bn) * p.batch,

@@ -192,7 +192,7 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
   const int LP = t.bm * t.cpr, LQ = t.bn * t.cpr, STAGE = LP + LQ;
   const int LDS = lds_chunks(t.bm, t.bn, t.cpr, t.st, es);
   const int ERC = epi_row_chunks(t.bn, es), SROW = ERC * EPC;
-  const int NW = t.wm * t.wn + t.lw, NIW = STAGE / 64 / NW;  // every wave issues loads and stores
+  const int NW = t.wm * t.wn, NIW = STAGE / 64 / NW;  // every wave issues loads and stores
 
   if (t.st * STAGE > LDS) fail(std::string(what) + ": the K-stage ring does not fit the LDS array");
   if (STAGE % (64 * NW) != 0 || LP % 64 != 0) fail(std::string(what) + ": stage does not split into wave loads");
@@ -234,7 +234,7 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
     else rect_decode(q, g.tiles_m, g.tiles_n, ti, tj);
     // the kernel's wave column (diagonal triangle tiles remap row half 1)
     auto wave_col = [&](int wm_, int wn_) {
-      const bool remap = tri && t.wm == 2 && t.wn == 4 && t.lw == 0 && !(t.bm == 256 && kind.p_nat);
+      const bool remap = tri && t.wm == 2 && t.wn == 4 && !(t.bm == 256 && kind.p_nat);
       return remap ? tri_wave_col(wm_, wn_, t.wn, ti == tj) : wn_;
     };
     if (slice >= g.batch || ti < 0 || tj < 0 || ti >= g.tiles_m || tj >= g.tiles_n || (tri && tj > ti)) {
@@ -280,9 +280,7 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
     // epilogue operands captured from the K stages (mirrors capture())
     const long long db0 = (long long)slice * g.d_bs;
     const int RCQ = t.bn / EPC;
-    // (a poly with loader waves captures nothing: its epilogue reads O_A)
-    const bool poly_reads_e = mode == MODE_POLY && t.lw > 0;
-    for (int kt = 0; kt < nk && mode != MODE_GRAM && !poly_reads_e; ++kt) {
+    for (int kt = 0; kt < nk && mode != MODE_GRAM; ++kt) {
       const int k0 = kt * BK, slot = kt % t.st;
       if (mode == MODE_POLY && kt >= nat_p) {
         bool any = false;
@@ -356,18 +354,6 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
               if (mode == MODE_POLY) {
                 access(g.d_in, (db + j) * 4, 16, what);
                 access(g.d_in, (db + i) * 4, 4, what);
-                if (poly_reads_e && !(ti == tj && j > i)) {  // (not read: see the kernel)
-                  const long long e0 = (long long)slice * g.e_bs + (long long)i * g.lde + j;
-                  access(g.E, e0 * es, qsz, what);
-                  // (a lower-triangle A: the element must be one the Gram stored)
-                  auto wr = g_written.find(reinterpret_cast<uintptr_t>(g.E));
-                  if (wr != g_written.end())
-                    for (int e = 0; e < qsz / es; ++e)
-                      if (wr->second[e0 + e] != 1) {
-                        fail(std::string(what) + ": poly epilogue reads an element of A the Gram did not write");
-                        break;
-                      }
-                }
               }
               for (int e = 0; e < 4; ++e)
                 if (i == j + e) {

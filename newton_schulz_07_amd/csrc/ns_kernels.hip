@@ -177,23 +177,21 @@ __device__ __forceinline__ int nat_lane_byte(int rb, int h, int lane, int rc, fl
   return nat_lane_byte_f32(rb, h, lane, rc);
 }
 
-// OCC workgroups of WM x WN + LW waves per CU: at least OCC (WM WN + LW) / 4
-// waves on each of the CU's four SIMDs (HIP's second launch bound), which
-// caps the VGPRs.
+// OCC workgroups of WM x WN waves per CU: at least OCC WM WN / 4 waves on
+// each of the CU's four SIMDs (HIP's second launch bound), which caps the
+// VGPRs.  Every wave runs MFMAs and issues its share of the K stages' loads.
 // NG > 1: the launch covers up to NG groups of slices of different shapes
 // (GemmLaunch); the workgroup's group is found from its logical tile id.
-// LW loader waves join the WM x WN MFMA waves: they issue their share of the
-// K stages' loads and the stores, nothing else.
-template <typename T, int BM, int BN, int WM, int WN, int LW, int CPR, int ST, int OCC, int MODE, int PL, int QL,
-          int NG, bool LATE>
-__global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4) void gemm_kernel(
+template <typename T, int BM, int BN, int WM, int WN, int CPR, int ST, int OCC, int MODE, int PL, int QL, int NG,
+          bool LATE>
+__global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_kernel(
     const GemmLaunch<NG> L) {
   // operand layouts (OperandLayout): which read paths each operand needs
   constexpr bool PNAT = PL == LAY_NAT, QNAT = QL == LAY_NAT;
   constexpr bool P_KC = PL != LAY_NAT, P_NT = PL != LAY_KCONT;  // K-contiguous / natural reads of P
   constexpr bool Q_KC = QL != LAY_NAT, Q_NT = QL != LAY_KCONT;
   constexpr bool HAS_SYM = PL == LAY_SYM || QL == LAY_SYM;
-  constexpr int NW = WM * WN + LW, NT = NW * 64;  // every wave of the workgroup
+  constexpr int NW = WM * WN, NT = NW * 64;  // every wave of the workgroup
   constexpr int EPC = Elem<T>::kChunk;
   constexpr int ES = (int)sizeof(T);
   constexpr int BK = CPR * EPC;
@@ -209,14 +207,13 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
   static_assert(CPR == 4 || CPR == 8 || CPR == 16, "4, 8 or 16 chunks per LDS row");
   static_assert(LP % 64 == 0 && STAGE % (64 * NW) == 0, "stage must split into whole wave loads");
   static_assert(ST >= 2 && NIW * (ST - 2) < 64, "ring depth");
-  static_assert(!LATE || (!mode_is_tri(MODE) && LW == 0), "late load issue: update tiles only");
+  static_assert(!LATE || !mode_is_tri(MODE), "late load issue: update tiles only");
 
   __shared__ uint4 lds[lds_chunks(BM, BN, CPR, ST, ES)];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool mw = LW == 0 || wave < WM * WN;  // an MFMA wave (wave-uniform)
-  const int wm = (mw ? wave : 0) / WN;
+  const int wm = wave / WN;
 
   int grp = 0, lin;
   if constexpr (NG > 1) lin = xcd_group_tile(blockIdx.x, gridDim.x, L.start, L.n, &grp);
@@ -232,8 +229,8 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
   // columns, and no MFMAs for blocks wholly above the diagonal (tri_wave_col).
   // Not the 256 tile on natural-layout operands (the tall Gram): it already
   // spills, and the skip made it slower.
-  constexpr bool DIAG_SKIP = mode_is_tri(MODE) && WM == 2 && WN == 4 && LW == 0 && !(BM == 256 && PL == LAY_NAT);
-  const int wn = DIAG_SKIP ? tri_wave_col(wm, (mw ? wave : 0) % WN, WN, ti == tj) : (mw ? wave : 0) % WN;
+  constexpr bool DIAG_SKIP = mode_is_tri(MODE) && WM == 2 && WN == 4 && !(BM == 256 && PL == LAY_NAT);
+  const int wn = DIAG_SKIP ? tri_wave_col(wm, wave % WN, WN, ti == tj) : wave % WN;
   uint32_t above = 0;  // bit a * SN + b: block (a, b) is not computed
   if (DIAG_SKIP && ti == tj) {
 #pragma unroll
@@ -418,7 +415,7 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
   // (LATE).  (The 128 x 128 triangle tiles, two workgroups per CU, lose
   // from it: their lower-triangle poly then spills.)
   constexpr bool STAGGER = (MODE == MODE_UPD_ROW || MODE == MODE_UPD_COL || (mode_is_tri(MODE) && BM == 256)) &&
-                           ST == 2 && LW == 0 && std::is_same<T, bf16>::value;
+                           ST == 2 && std::is_same<T, bf16>::value;
   const int issue_step = !STAGGER ? -1
                          : LATE   ? 0
                                   : (wm == 1 && (g.K + BK - 1) / BK >= kStaggerMinStages ? 0 : -1);
@@ -473,9 +470,7 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
   const float gram_scale = inv_norm * inv_norm;
   const float cb = g.cb, cc = g.cc;
   float drow[SM];
-  // with loader waves the poly's MFMA waves keep no O_A quads (registers):
-  // its epilogue reads O_A from memory instead
-  constexpr bool POLY_CAP = MODE == MODE_POLY && LW == 0;
+  constexpr bool POLY_CAP = MODE == MODE_POLY;  // O_A quads kept in registers
   QRaw obuf[POLY_CAP ? SM : 1][POLY_CAP ? SN : 1][4];
   if (MODE == MODE_UPD_ROW) {
 #pragma unroll
@@ -574,11 +569,10 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
       if (kt + ST - 1 < nk) issue(kt + ST - 1, (u + ST - 1) % ST);
     };
     if (issue_step < 0) late();
-    if (!mw) return;
     compute(u, pn, qn, late);
     // the poly's O_A capture happens at the stage covering the tile's own
     // columns, left of its diagonal, where P is K-contiguous
-    if constexpr (MODE != MODE_GRAM && !(MODE == MODE_POLY && (decltype(pn)::value || !POLY_CAP))) capture(u, kt);
+    if constexpr (MODE != MODE_GRAM && !(MODE == MODE_POLY && decltype(pn)::value)) capture(u, kt);
   };
   auto phase = [&](int kt_begin, int kt_end, auto pn, auto qn) __attribute__((always_inline)) {  // kt_begin % ST == 0
     int kt0 = kt_begin;
@@ -625,7 +619,7 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
   T* S = reinterpret_cast<T*>(lds);
   constexpr int SROW = ERC * EPC;  // staged row stride in elements
 
-  if (mw) {
+  {
 #pragma unroll
     for (int a = 0; a < SM; ++a) {
       const int il = wm * WTM + a * 32 + acc_i(lane);
@@ -649,16 +643,8 @@ __global__ __launch_bounds__((WM* WN + LW) * 64, (OCC * (WM * WN + LW) + 3) / 4)
               }
             }
           } else if (MODE == MODE_POLY) {
-            float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            if constexpr (POLY_CAP)
-              Quad<T>::unpack(obuf[a][b][rg], o);
-            else if (!(diag_tile && j > i))
-              // (a quad wholly above a diagonal tile's diagonal is replaced by
-              // the mirror of the lower half when stored: its O_A is not read,
-              // and with A stored as its lower block triangle it may not exist)
-              Quad<T>::unpack(*reinterpret_cast<const QRaw*>(reinterpret_cast<const T*>(g.E) + (size_t)slice * g.e_bs +
-                                                             (size_t)i * g.lde + j),
-                              o);
+            float o[4];
+            Quad<T>::unpack(obuf[POLY_CAP ? a : 0][POLY_CAP ? b : 0][rg], o);
             const float4 dj = *reinterpret_cast<const float4*>(din + j);
             const float dje[4] = {dj.x, dj.y, dj.z, dj.w};
             const float di = din[i];
@@ -934,12 +920,12 @@ static void dispatch(K kernel, dim3 grid, dim3 block, hipStream_t st, A... args)
 template <typename T, int MODE, int CLS, int PL, int QL, bool LATE = false>
 static hipError_t launch_mode(const GemmArgs* gs, int n, hipStream_t st) {
   constexpr TileCfg t = tile_cfg(std::is_same<T, bf16>::value ? 1 : 0, mode_is_tri(MODE), CLS);
-  const dim3 block((t.wm * t.wn + t.lw) * 64);
+  const dim3 block(t.wm * t.wn * 64);
   if (n == 1) {
     GemmLaunch<1> L{};
     L.g[0] = gs[0];
     L.n = 1;
-    dispatch(gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.lw, t.cpr, t.st, t.occ, MODE, PL, QL, 1, LATE>,
+    dispatch(gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.cpr, t.st, t.occ, MODE, PL, QL, 1, LATE>,
              dim3(gs[0].tiles_per_slice * gs[0].batch), block, st, L);
     return hipGetLastError();
   }
@@ -951,7 +937,7 @@ static hipError_t launch_mode(const GemmArgs* gs, int n, hipStream_t st) {
         n - g0, [&](int i) { return (long long)gs[g0 + i].tiles_per_slice * gs[g0 + i].batch; }, L.start, &total);
     for (int i = 0; i < k; ++i) L.g[i] = gs[g0 + i];
     L.n = k;
-    dispatch(gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.lw, t.cpr, t.st, t.occ, MODE, PL, QL, kMaxLaunchGroups, LATE>,
+    dispatch(gemm_kernel<T, t.bm, t.bn, t.wm, t.wn, t.cpr, t.st, t.occ, MODE, PL, QL, kMaxLaunchGroups, LATE>,
              dim3((unsigned)total), block, st, L);
     if (hipError_t e = hipGetLastError()) return e;
     g0 += k;

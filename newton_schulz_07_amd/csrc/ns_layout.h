@@ -34,7 +34,6 @@ NS_HD constexpr bool mode_is_tri(int mode) { return mode == MODE_GRAM || mode ==
 // for.
 struct TileCfg {
   int bm, bn, wm, wn, cpr, st, occ;
-  int lw = 0;  // loader waves: extra waves that only issue the K stages' loads and join the stores
 };
 
 #ifndef NS_TILE_BF16_TRI
@@ -320,9 +319,6 @@ struct GemmArgs {
   void* out_t;        // transposed output (mirror for Gram/poly, X'ᵀ), or null
   long long ot_bs;
   int ldt;
-  const void* E;      // epilogue matrix: O_A (poly) or X (update); unused for Gram
-  long long e_bs;
-  int lde;
   const float* d_in;  // diagonal vector read by the epilogue (poly: d_A, update: d_C)
   float* d_out;       // diagonal vector written (Gram: d_A, poly: d_C)
   long long d_bs;     // slice stride of both diagonal vectors

@@ -233,9 +233,6 @@ inline GemmArgs poly_args(const Plan& p, const TileChoice& tc, const void* oa, c
   g.out = g.out_t = oc;
   g.o_bs = g.ot_bs = p.m * p.m;
   g.ldo = g.ldt = (int)p.m;
-  g.E = oa;
-  g.e_bs = p.m * p.m;
-  g.lde = (int)p.m;
   g.d_in = da;
   g.d_out = dc;
   g.d_bs = p.m;
@@ -308,9 +305,6 @@ inline GemmArgs update_args(const Plan& p, const void* x, const void* oc, const 
   g.o_bs = p.rows * p.cols;
   g.ldo = (int)p.cols;
   g.out_t = nullptr;
-  g.E = x;
-  g.e_bs = p.rows * p.cols;
-  g.lde = (int)p.cols;
   g.d_in = dc;
   g.d_out = nullptr;
   g.d_bs = p.m;
