@@ -232,3 +232,22 @@ def test_timing_records_each_launch():
         ms, cnt = ns.ns_timing_query(kind)
         assert cnt == n and ms > 0, (kind, cnt)
     ns.ns_timing_reset()
+
+
+@pytest.mark.parametrize("shape,mode", [
+    ((1, 1024, 1024), "after-first-k-step"),   # 16 update tiles: at most four rounds
+    ((43, 1024, 1536), "staggered"),            # 1032 tiles, K = 1024: 16 K stages
+    ((43, 768, 2048), "after-first-k-step"),    # 1032 tiles, K = 768: 12 K stages, too short to stagger
+    ((43, 2048, 768), "after-first-k-step"),    # the same, tall (X' = X C)
+])
+def test_update_load_issue_mode(shape, mode):
+    # the bf16 update's load issue follows its launch's tile count and K; the
+    # outputs do not depend on it (only the time at which loads go out moves)
+    dev = device()
+    x = gaussian(shape, 1200, torch.bfloat16).to(dev)
+    y = ns.orthogonalize(x)
+    torch.cuda.synchronize()
+    cfg = ns.ns_query_last_config()
+    assert f"loads={mode}" in cfg, cfg
+    e = float(rel_err(to64(y[0]), newton_schulz(to64(x[0])))[0])
+    assert e <= 1e-2, e
