@@ -66,6 +66,22 @@ void access(const void* ptr, long long byte_off, int len, const char* what) {
          " outside " + it->second.name + " (" + std::to_string(it->second.bytes) + " bytes)");
 }
 
+// A whole aligned 16-byte block read from a 16-byte aligned buffer: it must
+// hold at least one byte of the buffer (it then lies in that byte's page; it
+// may run past the buffer's end by up to 15 bytes, never before its start).
+void access_block(const void* ptr, long long byte_off, const char* what) {
+  ++g_checks;
+  auto it = g_bufs.find(reinterpret_cast<uintptr_t>(ptr));
+  if (it == g_bufs.end()) {
+    fail(std::string(what) + ": pointer is not a registered buffer");
+    return;
+  }
+  if (reinterpret_cast<uintptr_t>(ptr) % 16 || byte_off % 16 || byte_off < 0 ||
+      (size_t)byte_off >= it->second.bytes)
+    fail(std::string(what) + ": block at " + std::to_string(byte_off) + " holds no byte of " + it->second.name +
+         " (" + std::to_string(it->second.bytes) + " bytes) or is misaligned");
+}
+
 void lds_index(int idx, int limit, const char* what) {
   ++g_checks;
   if (idx < 0 || idx >= limit)
@@ -566,15 +582,49 @@ void replay_pad(const PadArgs& g, int es, const char* what) {
         const long long padded_vec = (b * g.rows * vpr + v) * 16;
         if (g.to_padded) {
           access(g.dst, padded_vec, 16, what);
-          for (int k = 0; k < epv; ++k)
-            if (r < g.urows && j0 + k < g.ucols) access(g.src, ((b * g.urows + r) * g.ucols + j0 + k) * es, es, what);
-        } else {
-          if (j0 >= g.ucols) continue;  // a vector wholly in the padding is not read
-          access(g.src, padded_vec, 16, what);
-          for (int k = 0; k < epv; ++k)
-            if (j0 + k < g.ucols) access(g.dst, ((b * g.urows + r) * g.ucols + j0 + k) * es, es, what);
+          if (r < g.urows && j0 < g.ucols) {  // mirrors pad_sumsq_kernel
+            const long long n = std::min<long long>(epv, g.ucols - j0);
+            const long long a = ((b * g.urows + r) * g.ucols + j0) * es, sh = a % 16;
+            access(g.src, a, (int)(n * es), what);  // the elements the vector takes
+            access_block(g.src, a - sh, what);
+            // the second block, clamped to the block holding the array's last byte
+            const long long last = (g.batch * g.urows * g.ucols * es - 1) / 16 * 16;
+            access_block(g.src, std::min(a - sh + 16, last), what);
+            if (sh + n * es > 16 && a - sh + 16 > last) fail(std::string(what) + ": needed block past the last one");
+          }
         }
       }
+  if (g.to_padded) return;
+  // unpad: every 16-byte block of the caller's array (mirrors unpad_kernel)
+  const long long per_slice = g.urows * g.ucols, total = g.batch * per_slice;
+  for (long long e0 = 0; e0 < total; e0 += epv) {
+    long long sl = e0 / per_slice;
+    long long rr = e0 - sl * per_slice, i = rr / g.ucols, j = rr - i * g.ucols;
+    if (j + epv <= g.ucols && e0 + epv <= total) {  // one padded row: aligned blocks of it
+      const long long row = (sl * g.rows + i) * g.cols * es, sh = (j * es) % 16;
+      if (row % 16) fail(std::string(what) + ": padded row not 16-byte aligned");
+      access(g.src, row + j * es - sh, 16, what);
+      if (sh) access(g.src, row + j * es - sh + 16, 16, what);
+      if (row + j * es - sh + (sh ? 32 : 16) > row + g.cols * es) fail(std::string(what) + ": block outside its row");
+      access(g.dst, e0 * es, 16, what);
+      continue;
+    }
+    for (int k = 0; k < epv; ++k) {
+      if (e0 + k < total) {
+        if (i >= g.urows || j >= g.ucols || sl >= g.batch) fail(std::string(what) + ": element outside the block");
+        access(g.src, ((sl * g.rows + i) * g.cols + j) * es, es, what);
+        if (e0 + epv > total) access(g.dst, (e0 + k) * es, es, what);
+      }
+      if (++j == g.ucols) {
+        j = 0;
+        if (++i == g.urows) {
+          i = 0;
+          ++sl;
+        }
+      }
+    }
+    if (e0 + epv <= total) access(g.dst, e0 * es, 16, what);
+  }
 }
 
 // Replays one ns_orthogonalize call as the driver sequences it.

@@ -827,34 +827,94 @@ __global__ __launch_bounds__(kNormThreads) void scale_kernel(const NormArgs g) {
 
 // --------------------------------------------------- padding (odd shapes)
 
+// Bytes [sh, sh + 16) of the 32 bytes lo:hi (sh a multiple of 2, below 16).
+__device__ __forceinline__ uint4 bytes_at(uint4 lo, uint4 hi, unsigned sh) {
+  const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  const unsigned q = sh >> 2, b = sh & 3;
+  uint32_t win[5];  // dwords q .. q + 4
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const uint32_t a = (q & 1) ? w[k + 1] : w[k];
+    const uint32_t c = (q & 1) ? w[k + 3] : w[k + 2];
+    win[k] = (q & 2) ? c : a;
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[k] = __builtin_amdgcn_alignbyte(win[k + 1], win[k], b);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+// v with its bytes from nb on (nb a multiple of 2, below 16) set to zero.
+__device__ __forceinline__ uint4 keep_bytes(uint4 v, unsigned nb) {
+  uint32_t o[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int left = (int)nb - 4 * k;  // bytes of dword k to keep
+    o[k] = left >= 4 ? o[k] : left <= 0 ? 0u : (o[k] & 0xffffu);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // The zero-padded copy of a slice and its partial sums of squares in one
 // pass.  Block (chunk, slice) covers the same vectors of the padded slice,
 // thread by thread, as sumsq_kernel does over the padded copy, so the
-// partials are bitwise the ones that kernel would compute from it; each
-// vector is gathered element by element from the caller's rows (not 16-byte
-// aligned), zero outside them.
+// partials are bitwise the ones that kernel would compute from it.  The
+// caller's rows are not 16-byte aligned: each vector's elements are taken
+// from the one or two aligned 16-byte blocks of the caller's array that hold
+// them, read whole and shifted into place, and zeroed past the row's end.
+// (The array starts 16-byte aligned, so each such block holds a byte of the
+// array; its last block may run up to 14 bytes past the end, in the same
+// page.)
 template <typename T>
 __global__ __launch_bounds__(kNormThreads) void pad_sumsq_kernel(const PadArgs p, const NormArgs g) {
   __shared__ float red[kNormThreads / 64];
-  constexpr int EPV = Elem<T>::kChunk;
+  constexpr int EPV = Elem<T>::kChunk, ES = (int)sizeof(T);
   const int slice = blockIdx.y, chunk = blockIdx.x;
-  const T* src = reinterpret_cast<const T*>(p.src) + (size_t)slice * p.urows * p.ucols;
+  const char* src = reinterpret_cast<const char*>(p.src) + (size_t)slice * p.urows * p.ucols * ES;
   uint4* dst = reinterpret_cast<uint4*>(p.dst) + (size_t)slice * g.slice_vecs;
   const int vpr = (int)(p.cols / EPV), urows = (int)p.urows, ucols = (int)p.ucols;
   const int v0 = (int)((long long)chunk * g.chunk_vecs);
   const int v1 = (int)((v0 + g.chunk_vecs < g.slice_vecs) ? v0 + g.chunk_vecs : g.slice_vecs);
+  // the aligned block holding the array's last byte: the second block of a
+  // vector is read from no further than here (beyond it, its bytes are unused)
+  const uint4* last = reinterpret_cast<const uint4*>(
+      (reinterpret_cast<uintptr_t>(p.src) + (size_t)p.batch * p.urows * p.ucols * ES - 1) & ~(uintptr_t)15);
+  // four vectors per round: every load of a round is issued before the first
+  // is used (the sum still runs over the vectors in order)
+  constexpr int U = 4;
   float s = 0.0f;
-  for (int v = v0 + (int)threadIdx.x; v < v1; v += kNormThreads) {
-    int i, j0;
-    pad_vec(v, vpr, EPV, &i, &j0);
-    T e[EPV];
+  for (int vb = v0 + (int)threadIdx.x; vb < v1; vb += U * kNormThreads) {
+    uint4 lo[U], hi[U];
+    unsigned sh[U], nb[U];
 #pragma unroll
-    for (int k = 0; k < EPV; ++k)
-      e[k] = (i < urows && j0 + k < ucols) ? src[(size_t)i * ucols + j0 + k] : T(0.0f);
-    uint4 val;
-    __builtin_memcpy(&val, e, 16);
-    dst[v] = val;
-    s += sumsq16(val, T());
+    for (int u = 0; u < U; ++u) {
+      const int v = vb + u * kNormThreads;
+      int i, j0;
+      pad_vec(v, vpr, EPV, &i, &j0);
+      lo[u] = hi[u] = make_uint4(0u, 0u, 0u, 0u);
+      sh[u] = 0;
+      nb[u] = 0;  // bytes of the caller's row in this vector (0: none)
+      if (v < v1 && i < urows && j0 < ucols) {
+        const int n = ucols - j0 < EPV ? ucols - j0 : EPV;
+        const char* a = src + ((size_t)i * ucols + j0) * ES;
+        sh[u] = (unsigned)(reinterpret_cast<uintptr_t>(a) & 15);
+        nb[u] = (unsigned)(n * ES);
+        const uint4* al = reinterpret_cast<const uint4*>(a - sh[u]);
+        lo[u] = al[0];
+        hi[u] = al + 1 < last ? al[1] : *last;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = vb + u * kNormThreads;
+      if (v >= v1) break;
+      uint4 val = make_uint4(0u, 0u, 0u, 0u);
+      if (nb[u]) {
+        val = bytes_at(lo[u], hi[u], sh[u]);
+        if (nb[u] < 16) val = keep_bytes(val, nb[u]);
+      }
+      dst[v] = val;
+      s += sumsq16(val, T());
+    }
   }
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
@@ -867,27 +927,58 @@ __global__ __launch_bounds__(kNormThreads) void pad_sumsq_kernel(const PadArgs p
   }
 }
 
-// The caller's block out of a padded result: one 16-byte vector of the
-// padded slice's first urows rows per thread (grid-stride in x, slice in y),
-// its elements inside the caller's columns stored one by one.
+// The caller's block out of a padded result.  The caller's array is taken as
+// one flat run of 16-byte blocks (it starts 16-byte aligned): one block per
+// thread (grid-stride in x over the blocks whose first element lies in slice
+// blockIdx.y), stored whole, or element by element where it runs past the
+// array's end.  A block whose elements lie in one row of the padded
+// slice (rows 16-byte aligned there) takes them from the one or two aligned
+// 16-byte blocks of that row that hold them; one that spans two rows gathers
+// them element by element.
 template <typename T>
 __global__ __launch_bounds__(256) void unpad_kernel(const PadArgs p) {
-  constexpr int EPV = Elem<T>::kChunk;
-  const int slice = blockIdx.y;
-  const int vpr = (int)(p.cols / EPV), ucols = (int)p.ucols;
-  const int nv = (int)p.urows * vpr;
-  const uint4* src = reinterpret_cast<const uint4*>(p.src) + (size_t)slice * p.rows * vpr;
-  T* dst = reinterpret_cast<T*>(p.dst) + (size_t)slice * p.urows * p.ucols;
-  for (int v = blockIdx.x * 256 + (int)threadIdx.x; v < nv; v += gridDim.x * 256) {
-    int i, j0;
-    pad_vec(v, vpr, EPV, &i, &j0);
-    if (j0 >= ucols) continue;
-    const uint4 val = src[v];
+  constexpr int EPV = Elem<T>::kChunk, ES = (int)sizeof(T);
+  const long long per_slice = p.urows * p.ucols, total = p.batch * per_slice;
+  const int urows = (int)p.urows, ucols = (int)p.ucols;
+  const T* src = reinterpret_cast<const T*>(p.src);
+  T* dst = reinterpret_cast<T*>(p.dst);
+  const long long base = (long long)blockIdx.y * per_slice;           // the slice's first element
+  const long long b0 = (base + EPV - 1) / EPV, b1 = (base + per_slice + EPV - 1) / EPV;
+  for (long long blk = b0 + (long long)blockIdx.x * 256 + threadIdx.x; blk < b1; blk += (long long)gridDim.x * 256) {
+    const long long e0 = blk * EPV;
+    long long sl = blockIdx.y;
+    const int r = (int)(e0 - base);
+    int i = r / ucols, j = r - i * ucols;
+    if (j + EPV <= ucols && e0 + EPV <= total) {
+      const char* row = reinterpret_cast<const char*>(src + (sl * p.rows + i) * p.cols);
+      const unsigned sh = (unsigned)(j * ES) & 15u;
+      const uint4* al = reinterpret_cast<const uint4*>(row + (j * ES - (int)sh));
+      const uint4 lo = al[0];
+      const uint4 hi = sh ? al[1] : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(dst + e0) = bytes_at(lo, hi, sh);
+      continue;
+    }
     T e[EPV];
-    __builtin_memcpy(e, &val, 16);
 #pragma unroll
-    for (int k = 0; k < EPV; ++k)
-      if (j0 + k < ucols) dst[(size_t)i * ucols + j0 + k] = e[k];
+    for (int k = 0; k < EPV; ++k) {
+      e[k] = e0 + k < total ? src[(sl * p.rows + i) * p.cols + j] : T(0.0f);
+      if (++j == ucols) {
+        j = 0;
+        if (++i == urows) {
+          i = 0;
+          ++sl;
+        }
+      }
+    }
+    if (e0 + EPV <= total) {
+      uint4 val;
+      __builtin_memcpy(&val, e, 16);
+      *reinterpret_cast<uint4*>(dst + e0) = val;
+    } else {
+#pragma unroll
+      for (int k = 0; k < EPV; ++k)
+        if (e0 + k < total) dst[e0 + k] = e[k];
+    }
   }
 }
 
@@ -1016,9 +1107,10 @@ hipError_t launch_pad_sumsq(int dtype, const PadArgs& p, const NormArgs& g, int 
 }
 
 hipError_t launch_unpad(int dtype, const PadArgs& p, hipStream_t st) {
-  const long long vecs = p.urows * (p.cols / elems_per_chunk(dtype));
-  const long long want = (vecs + 255) / 256;
-  const unsigned bx = (unsigned)(want < 4096 ? (want > 0 ? want : 1) : 4096);
+  const int epv = elems_per_chunk(dtype);
+  const long long blocks = (p.urows * p.ucols + epv - 1) / epv + 1;  // 16-byte blocks starting in one slice
+  const long long want = (blocks + 255) / 256;
+  const unsigned bx = (unsigned)(want < 65536 ? want : 65536);
   if (dtype == 1) dispatch(unpad_kernel<bf16>, dim3(bx, (unsigned)p.batch), dim3(256), st, p);
   else dispatch(unpad_kernel<float>, dim3(bx, (unsigned)p.batch), dim3(256), st, p);
   return hipGetLastError();
