@@ -92,7 +92,11 @@ enum {
  *   stream    hipStream_t as void*.
  *
  * Each slice is normalised by its own Frobenius norm.  An all-zero slice
- * yields zeros.  NaN/Inf inputs propagate; they are not checked.
+ * yields zeros.  NaN/Inf inputs propagate; they are not checked.  The sum
+ * of squares and the first Gram product accumulate the raw input in fp32
+ * (the 1/||X|| scaling is applied in their epilogues), so a slice whose
+ * ||X||_F exceeds about 1.8e19 (its sum of squares past the fp32 range)
+ * gives no meaningful result (NaN or zeros).
  * Internally the Gram matrix A and the polynomial C = aI + bA + cAA are held
  * as an off-diagonal matrix (zero diagonal) in `dtype` plus an fp32 diagonal
  * vector; only lower-triangle tiles of both are computed.  C is mirrored;
