@@ -246,7 +246,7 @@ void replay_gemm(const GemmArgs& g, const StageKind& kind, int dtype, bool cover
     seen[lin] = 1;
     const int slice = lin / g.tiles_per_slice, q = lin - slice * g.tiles_per_slice;
     int ti, tj;
-    if (tri) tri_decode(q, ti, tj);
+    if (tri) tri_decode(q, g.tiles_m, ti, tj);
     else rect_decode(q, g.tiles_m, g.tiles_n, ti, tj);
     // the kernel's wave column (diagonal triangle tiles remap row half 1)
     auto wave_col = [&](int wm_, int wn_) {
@@ -832,6 +832,21 @@ void check_group_map() {
 
 // The diagonal tiles' wave columns are a permutation within each row half,
 // and the blocks they skip lie wholly above the diagonal.
+// tri_decode maps the tiles of every triangle size onto the lower triangle
+// one to one
+void check_tri_decode() {
+  for (int T = 1; T <= 300; ++T) {
+    std::vector<char> seen((size_t)T * T, 0);
+    const int n = T * (T + 1) / 2;
+    for (int q = 0; q < n; ++q) {
+      int ti = -1, tj = -1;
+      tri_decode(q, T, ti, tj);
+      if (ti < 0 || ti >= T || tj < 0 || tj > ti || seen[(size_t)ti * T + tj]++)
+        fail("tri_decode: tile " + std::to_string(q) + " of " + std::to_string(T) + " rows maps wrongly");
+    }
+  }
+}
+
 void check_diag_waves() {
   for (int wm = 0; wm < 2; ++wm) {
     int seen = 0;
@@ -864,6 +879,7 @@ void check_diag_waves() {
 
 int main(int argc, char** argv) {
   check_group_map();
+  check_tri_decode();
   check_diag_waves();
   // grouped call: --group dtype steps b r c [b r c ...]
   if (argc >= 7 && std::string(argv[1]) == "--group" && (argc - 4) % 3 == 0) {

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
   const int slice = lin / g.tiles_per_slice;
   const int q = lin - slice * g.tiles_per_slice;
   int ti, tj;
-  if (mode_is_tri(MODE)) tri_decode(q, ti, tj);
+  if (mode_is_tri(MODE)) tri_decode(q, g.tiles_m, ti, tj);
   else rect_decode(q, g.tiles_m, g.tiles_n, ti, tj);
   const int i0 = ti * BM, j0 = tj * BN;
   // diagonal triangle tiles with 2 x 4 MFMA waves: SIMD-balanced wave

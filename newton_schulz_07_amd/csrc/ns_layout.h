@@ -130,13 +130,37 @@ NS_HD int xcd_remap(int w, int G) {
                      : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
-// q-th tile of a lower triangle, row by row: (0,0) (1,0) (1,1) (2,0) ...
-NS_HD void tri_decode(int q, int& ti, int& tj) {
-  int i = (int)((__builtin_sqrtf(8.0f * (float)q + 1.0f) - 1.0f) * 0.5f);
-  while (i > 0 && i * (i + 1) / 2 > q) --i;
-  while ((i + 1) * (i + 2) / 2 <= q) ++i;
-  ti = i;
-  tj = q - i * (i + 1) / 2;
+// q-th tile of a lower triangle of T tile rows, in bands of kTriBand tile
+// rows walked column by column, so that a run of consecutive tiles (what one
+// XCD runs together, as xcd_remap hands each XCD a contiguous range) covers
+// a few tile rows and several columns: few operand panels per XCD's L2.
+// Band b0 (rows b0 .. b0 + h - 1, h = min(kTriBand, T - b0)) holds the b0 h
+// tiles left of its diagonal block, column by column, then the h (h + 1) / 2
+// tiles of that block, column by column.
+constexpr int kTriBand = 8;
+NS_HD void tri_decode(int q, int T, int& ti, int& tj) {
+  int b0 = 0;
+  for (;;) {
+    const int h = T - b0 < kTriBand ? T - b0 : kTriBand;
+    const int n = b0 * h + h * (h + 1) / 2;
+    if (q < n || b0 + h >= T) {
+      if (q < b0 * h) {
+        tj = q / h;
+        ti = b0 + q % h;
+      } else {
+        int r = q - b0 * h, c = 0;
+        while (r >= h - c) {
+          r -= h - c;
+          ++c;
+        }
+        tj = b0 + c;
+        ti = b0 + c + r;
+      }
+      return;
+    }
+    q -= n;
+    b0 += h;
+  }
 }
 
 // q-th tile of a tiles_m x tiles_n rectangle, in groups of 8 tile rows
