@@ -301,7 +301,7 @@ SAMPLES = {"experts16_1536x2048": [0, 7, 15], "experts128_1536x2048": [0, 63, 12
 
 
 def all_configs(prefix, steps, warmup):
-    """Every workload: ms/call (and spread) of this build and of the dense
+    """Every workload: ms/call (and spread) of this library and of the dense
     comparator, effective TFLOP/s against the spec and the measured peak, and
     both outputs' relative error vs the fp64 oracle on sampled slices beside
     the rounding-model floor.  Writes prefix.json and prefix.md."""
@@ -363,7 +363,7 @@ def all_configs(prefix, steps, warmup):
                   indent=1)
     lines = ["# ns_orthogonalize on every workload: time, accuracy, the dense comparator, grouped calls, odd sides",
              "", "Command (MI355X, one GPU; `$REPO` is the repository root):", "", "```",
-             f"python $REPO/bench.py --all-configs $REPO/gpurun_out/prof/all_configs --warmup {warmup} --steps {steps}",
+             f"python $REPO/bench.py --all-configs {prefix} --warmup {warmup} --steps {steps}",
              "```", "",
              f"This box: register-only MFMA loop {peak['tflops']:.0f} TFLOP/s at a {peak['shader_clock_mhz']:.0f} MHz "
              f"shader clock; {host['cores']} host cores ({host['cpu_model']}).  Kernel source hash "
@@ -486,7 +486,7 @@ def main():
                     help="seconds of back-to-back calls after the timed region, split over the workloads "
                          "(reported under 'sustained'; 0: skip)")
     ap.add_argument("--all-configs", metavar="OUT_PREFIX",
-                    help="time and check every workload (this build's and the dense comparator's error vs "
+                    help="time and check every workload (this library's and the dense comparator's error vs "
                          "the oracle on sampled slices), write OUT_PREFIX.md and OUT_PREFIX.json, and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 64 MiB device copy three times (the reference that scales "
@@ -494,7 +494,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(stacks shard by whole slices across GPUs; see the design notes).", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
