@@ -238,3 +238,27 @@ def test_noalloc_rejects_bad_arguments_and_oversized_calls_before_any_launch():
         assert "fixed scratch" in L.ns_last_error().decode()
     assert L.ns_status_string(7).decode().startswith("NS_ERR_SCRATCH")
     assert ns.ns_workspace_bytes(1, 4096, 4096, 1) <= ns.NS_NOALLOC_SCRATCH_BYTES
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    # no fallback: without the built library every call raises
+    monkeypatch.setattr(ns, "LIB_PATH", "/nonexistent/libns_hip.so")
+    monkeypatch.setattr(ns, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        ns.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        ns.ns_workspace_bytes(1, 64, 64, 1)
+
+
+@pytest.mark.parametrize("call", ["orthogonalize", "orthogonalize_grouped", "ns_orthogonalize_noalloc"])
+def test_host_tensors_are_refused(call):
+    # the path runs on the GPU only: a host tensor is an error, never computed on the CPU
+    import torch
+    x = torch.randn(2, 16, 24)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        if call == "orthogonalize":
+            ns.orthogonalize(x)
+        elif call == "orthogonalize_grouped":
+            ns.orthogonalize_grouped([x])
+        else:
+            ns.ns_orthogonalize_noalloc(x, torch.empty_like(x))
