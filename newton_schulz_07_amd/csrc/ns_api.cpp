@@ -253,7 +253,7 @@ void record_config(const Plan& p, int steps) {
                 p.tall ? "rows" : "columns(transposed-read)",
                 ns::late_issue(p.dtype, (long long)ns::tiles_of(p.rows, tr.bm) * ns::tiles_of(p.cols, tr.bn) * p.batch,
                                (int)p.m)
-                    ? "after-first-k-step"
+                    ? "after-k-steps-0-1"
                     : (p.dtype == NS_DTYPE_BF16 && ns::update_k_stages((int)p.m) >= ns::kStaggerMinStages
                            ? "staggered"
                            : "stage-start"));

@@ -296,7 +296,10 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
   // inside K (always, for K a multiple of BK) only rows past M / N need the
   // zero fill, and their offset already starts past the slice end; otherwise
   // each lane also checks its own k position.
-  auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
+  // part: -1 every load of the wave, 0 / 1 the first / second half of them
+  auto issue = [&](int kt, int slot, auto part) __attribute__((always_inline)) {
+    constexpr int PART = decltype(part)::value;
+    auto mine = [&](int t) __attribute__((always_inline)) { return PART < 0 || (t < NIW / 2) == (PART == 0); };
     const int k0 = kt * BK;
     // natural-layout reads this stage (compile-time unless LAY_SYM)
     const bool pn = PL == LAY_SYM ? kt >= nat_from_p : PNAT;
@@ -318,6 +321,7 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
     } else if (k0 + BK <= g.K) {
 #pragma unroll
       for (int t = 0; t < NIW; ++t) {
+        if (!mine(t)) continue;
         const int idx = wave * NIW + t;  // wave-uniform
         const bool is_p = idx * 64 < LP;
         dma16(lds_addr(lds + slot * STAGE + idx * 64), off_of(t, is_p), is_p ? rP : rQ);
@@ -325,6 +329,7 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
     } else {
 #pragma unroll
       for (int t = 0; t < NIW; ++t) {
+        if (!mine(t)) continue;
         const int idx = wave * NIW + t;
         const bool is_p = idx * 64 < LP;
         const int kpos = dma_src(idx, lane, BM, BN, CPR, EPC, pn, qn, ES).kpos;
@@ -411,16 +416,18 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
   // the two waves of a SIMD then take turns, one issuing loads while the
   // other keeps the matrix core busy.  With fewer than 16 K stages the
   // later half of each stage's loads lands too late, and update launches of
-  // up to four rounds issue every wave's loads after the first k step
-  // (LATE).  (The 128 x 128 triangle tiles, two workgroups per CU, lose
-  // from it: their lower-triangle poly then spills.)
+  // up to four rounds issue each wave's loads later (LATE): the first half
+  // after k step 0, the second after k step 1.  (The 128 x 128 triangle
+  // tiles, two workgroups per CU, lose from it: their lower-triangle poly
+  // then spills.)
   constexpr bool STAGGER = (MODE == MODE_UPD_ROW || MODE == MODE_UPD_COL || (mode_is_tri(MODE) && BM == 256)) &&
                            ST == 2 && std::is_same<T, bf16>::value;
-  const int issue_step = !STAGGER ? -1
-                         : LATE   ? 0
-                                  : (wm == 1 && (g.K + BK - 1) / BK >= kStaggerMinStages ? 0 : -1);
+  constexpr bool SPLIT = LATE && STAGGER;  // (the fp32 instances never take LATE)
+  static_assert(!SPLIT || (KS >= 2 && NIW % 2 == 0), "late issue: two k steps, an even load count");
+  const int issue_step = !STAGGER || LATE ? -1 : (wm == 1 && (g.K + BK - 1) / BK >= kStaggerMinStages ? 0 : -1);
   // fragments of step s + 1 are read while the MFMAs of step s run
-  // `late` issues the next stage's loads after the MFMAs of k step issue_step
+  // `late` issues the next stage's loads (or half of them) after the MFMAs
+  // of k step issue_step (LATE: k steps 0 and 1)
   auto compute = [&](int slot, auto pn, auto qn, auto&& late) __attribute__((always_inline)) {
     uint4 pf[2][SM], qf[2][SN];
     load_step(slot, 0, pn, qn, pf[0], qf[0]);
@@ -434,9 +441,14 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
 #pragma unroll
         for (int b = 0; b < SN; ++b)
           if (!DIAG_SKIP || !((above >> (a * SN + b)) & 1u)) mfma_chunk(acc[a][b], qf[s & 1][b], pf[s & 1][a], T());
-      if (STAGGER && s == issue_step) {
+      if (SPLIT && s < 2) {
         __builtin_amdgcn_sched_barrier(0);
-        late();
+        if (s == 0) late(std::integral_constant<int, 0>());
+        else late(std::integral_constant<int, 1>());
+        __builtin_amdgcn_sched_barrier(0);
+      } else if (STAGGER && s == issue_step) {
+        __builtin_amdgcn_sched_barrier(0);
+        late(std::integral_constant<int, -1>());
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -565,10 +577,10 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
     else wait_vm_lgkm0<0>();
     ring_barrier();
     // the stage's loads go out here, or after the k step issue_step
-    auto late = [&]() __attribute__((always_inline)) {
-      if (kt + ST - 1 < nk) issue(kt + ST - 1, (u + ST - 1) % ST);
+    auto late = [&](auto part) __attribute__((always_inline)) {
+      if (kt + ST - 1 < nk) issue(kt + ST - 1, (u + ST - 1) % ST, part);
     };
-    if (issue_step < 0) late();
+    if (issue_step < 0 && !SPLIT) late(std::integral_constant<int, -1>());
     compute(u, pn, qn, late);
     // the poly's O_A capture happens at the stage covering the tile's own
     // columns, left of its diagonal, where P is K-contiguous
@@ -586,7 +598,7 @@ __global__ __launch_bounds__(WM* WN * 64, (OCC * WM * WN + 3) / 4) void gemm_ker
   };
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s)
-    if (s < nk) issue(s, s);
+    if (s < nk) issue(s, s, std::integral_constant<int, -1>());
   if constexpr (PL == LAY_SYM && QL == LAY_SYM) {
     // both operands symmetric: a lower-triangle tile (j0 <= i0) switches Q
     // to natural-layout reads first

@@ -235,10 +235,10 @@ def test_timing_records_each_launch():
 
 
 @pytest.mark.parametrize("shape,mode", [
-    ((1, 1024, 1024), "after-first-k-step"),   # 16 update tiles: at most four rounds
-    ((43, 1024, 1536), "staggered"),            # 1032 tiles, K = 1024: 16 K stages
-    ((43, 768, 2048), "after-first-k-step"),    # 1032 tiles, K = 768: 12 K stages, too short to stagger
-    ((43, 2048, 768), "after-first-k-step"),    # the same, tall (X' = X C)
+    ((1, 1024, 1024), "after-k-steps-0-1"),     # 16 update tiles: at most four rounds
+    ((43, 1024, 1536), "staggered"),             # 1032 tiles, K = 1024: 16 K stages
+    ((43, 768, 2048), "after-k-steps-0-1"),     # 1032 tiles, K = 768: 12 K stages, too short to stagger
+    ((43, 2048, 768), "after-k-steps-0-1"),     # the same, tall (X' = X C)
 ])
 def test_update_load_issue_mode(shape, mode):
     # the bf16 update's load issue follows its launch's tile count and K; the
